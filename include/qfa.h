@@ -1,0 +1,202 @@
+/*
+ * qfa — INT8-QK / BF16-PV flash attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libqfa.so. Every entry point takes plain pointers and sizes and
+ * returns a status code. All tensor pointers are DEVICE pointers owned by the
+ * caller; the library allocates no device memory, keeps no state besides a
+ * thread-local error message, and never synchronises: kernels are enqueued on
+ * the caller's HIP stream (`stream`, a hipStream_t; NULL is the default
+ * stream) and results are ready once that stream has completed them.
+ *
+ * Errors: every argument check runs on the host before any launch, so a call
+ * that returns an error has launched nothing and written nothing. A device
+ * fault, if one happens, surfaces at the caller's next synchronisation.
+ *
+ * Logical layouts. A "[B,H,S,D] tensor with strides (sb, sh, ss)" holds
+ * element (b,h,s,d) at base + b*sb + h*sh + s*ss + d, strides counted in
+ * elements; the channel stride is always 1. This covers contiguous BHSD as
+ * well as BSHD-backed views (sb = S*H*D, sh = D, ss = H*D). Quantized Q/K,
+ * scales, means, LSE and index arrays are always contiguous.
+ *
+ * Method (sources are the web pages this operation is described on):
+ *  - FastVideo API docs, "minimax_h3_sparse_int8" (module description and the
+ *    sparse_sm89_attention listing): K mean over the valid tokens, K centring
+ *    as a softmax-invariant shift, per-token int8 Q/K with fp32 scales, int8
+ *    QK with fp32 accumulation, BF16 PV, a tile-64 block mask with a per-tile
+ *    validity vector, one V scale per (head, channel) applied in the epilogue,
+ *    quantized Q/K and the output contiguous BHSD, BSHD views accepted.
+ *  - comfy-kitchen issue #177 (measurement table, observations, Question 2):
+ *    an additive per-key bias [1,1,1,K] shared by heads and queries, and the
+ *    core/skirt split whose partial softmaxes merge exactly through the LSE.
+ *  - ROCm/FlyDSL PR #886 ("Public API", "Kernel implementation"): the LSE is
+ *    fp32 [B,H,Sq], natural log, includes the softmax scale, is -inf for fully
+ *    masked rows, is written once per row, and is requested by passing the
+ *    output buffer (a caller-owned lse= out parameter).
+ *  - model-kernels issue #3 (maintainer reply): symmetric [-127,127] codes;
+ *    every score dequantized with its own row and key scales.
+ */
+#ifndef QFA_H
+#define QFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QFA_OK 0
+#define QFA_ERR_INVALID_ARG 1 /* a null/misaligned pointer, bad size, stride or combination */
+#define QFA_ERR_UNSUPPORTED 2 /* valid request this build does not implement (e.g. D not in {64,128}) */
+#define QFA_ERR_HIP 3         /* the HIP runtime rejected a launch */
+
+/* Element types. */
+#define QFA_BF16 1
+#define QFA_FP16 2
+#define QFA_FP32 3
+
+#define QFA_MAX_SEGMENTS 4
+
+/* Version of this ABI (major*100 + minor). */
+int qfa_version(void);
+
+/* Static description of a status code. */
+const char* qfa_status_string(int status);
+
+/* Detail of the last failed call made by this thread ("" if none). */
+const char* qfa_last_error(void);
+
+/*
+ * qfa_quantize_workspace_bytes — device workspace qfa_quantize_qk needs for
+ * the K mean (fp64 partial sums). Writes the byte count to *bytes.
+ */
+int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, size_t* bytes);
+
+/*
+ * qfa_quantize_qk — K mean, K centring and per-token symmetric int8
+ * quantization of Q and K (FastVideo "minimax_h3_sparse_int8": module
+ * description and the K-mean / _quantize_qk steps of sparse_sm89_attention;
+ * model-kernels issue #3: symmetric range).
+ *
+ * For every row x of Q, and of K - mu when center_k != 0:
+ *   a = max_c |x_c|;
+ *   a < 127*FLT_MIN  -> codes 0, scale 0;
+ *   else scale = fp32(a / 127), inv = fp32(127 / a),
+ *        code_c = clamp(round_half_even(fp32(x_c * inv)), -127, 127).
+ * mu[b,h,c] = fp32( fp64( exact sum over valid keys of K[b,h,j,c] ) / n ),
+ * n = Sk, or max(1, sum(vbs)) when vbs is given; K - mu is one fp32
+ * subtraction. qmu[b,h,i] = sum_c Q[b,h,i,c]*mu[b,h,c] (fp32) lets attn_fwd
+ * report the LSE of the uncentred scores.
+ *
+ * q, k:    [B,H,Sq,D] / [B,H,Sk,D] of `dtype` (QFA_BF16 or QFA_FP16), strides
+ *          as above; base and row strides 16-byte aligned.
+ * vbs:     nullable; int32[Sk/64] per-tile valid-token counts in [0,64]
+ *          (requires Sq == Sk, a multiple of 64). Pad rows (j mod 64 >=
+ *          vbs[j/64]) of Q and K get codes 0 and scale 0 and are left out of
+ *          the mean.
+ * center_k: 0 = no centring (kmean, qmu unused and may be NULL).
+ * q8, k8:  int8 [B,H,Sq,D] / [B,H,Sk,D] contiguous outputs.
+ * qs, ks:  fp32 [B,H,Sq] / [B,H,Sk] contiguous outputs.
+ * kmean:   fp32 [B,H,D] output (required when center_k).
+ * qmu:     nullable fp32 [B,H,Sq] output (only when center_k).
+ * workspace: device buffer of at least qfa_quantize_workspace_bytes(...)
+ *          bytes, 16-byte aligned (may be NULL when center_k == 0).
+ * D must be 64 or 128.
+ */
+int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                    const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                    const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                    const int32_t* vbs, int center_k,
+                    int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qfa_blockmask_to_index — tile mask to per-query-tile key-tile lists
+ * (FastVideo "minimax_h3_sparse_int8", sparse_sm89_attention: map_to_index).
+ *
+ * mask:  uint8 [B,H,Tq,Tk] contiguous, nonzero = query tile attends key tile.
+ * index: int32 [B,H,Tq,Tk] contiguous output; entries [0, count) of each row
+ *        hold the attended key tiles in ascending order, the rest are left
+ *        unwritten.
+ * count: int32 [B,H,Tq] contiguous output.
+ */
+int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
+                           int32_t* index, int32_t* count, void* stream);
+
+/*
+ * qfa_attn_fwd — attention forward on int8 Q/K codes and bf16/fp16 V
+ * (FastVideo "minimax_h3_sparse_int8"; comfy-kitchen issue #177; FlyDSL
+ * PR #886 for the LSE).
+ *
+ * For each row i of each (b,h) and each key j the call attends:
+ *   s_ij = sm_scale * qs_i * ks_j * (q8_i . k8_j) + bias_j       (natural log)
+ *   O_i  = v_scale[h,:] * sum_j softmax_j(s_ij) V_j
+ *   LSE_i = log sum_j exp(s_ij) + sm_scale * qmu_i
+ * The int8 dot is exact in int32; the softmax runs online in fp32 (log2
+ * domain) with P rounded to V's type for the PV product (fp32 accumulation).
+ * Key j is attended when it lies in one of the segments and, for block-sparse
+ * calls, its tile is listed for the query's tile and j mod 64 < vbs[j/64];
+ * a bias of -inf also excludes it. A row with no attended key gives O = 0 and
+ * LSE = -inf.
+ *
+ * q8, qs:   int8 [B,H,Sq,D], fp32 [B,H,Sq] (from qfa_quantize_qk).
+ * qmu:      nullable fp32 [B,H,Sq]; when given, sm_scale*qmu is added to the
+ *           LSE (pass it whenever K was centred and the LSE is requested).
+ * k8, ks:   int8 [B,H,Sk,D], fp32 [B,H,Sk].
+ * v:        [B,H,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
+ *           v_sh, v_ss); base and row strides 16-byte aligned.
+ * sm_scale: softmax scale (typically D^-0.5).
+ * bias:     nullable additive per-key bias of bias_dtype (QFA_FP32, QFA_BF16
+ *           or QFA_FP16), element (b,h,j) at bias + b*bias_sb + h*bias_sh + j;
+ *           pass 0 for a broadcast batch/head stride. It is shared by every
+ *           query row (a [B|1,H|1,1,K] tensor or a stride-0 expansion of one).
+ * index, count, vbs: block-sparse mode when index != NULL: int32 [B,H,T,T],
+ *           int32 [B,H,T], int32 [T] (from qfa_blockmask_to_index; vbs may be
+ *           NULL for full tiles), T = Sq/64 = Sk/64. Not combinable with bias.
+ * v_scale:  nullable fp32 [H,D] per-(head,channel) factor applied to O.
+ * nseg, seg: host array of nseg (<= 4) (start, length) pairs of key ranges,
+ *           ascending and disjoint; nseg = 0 means the whole [0, Sk).
+ * out:      [B,H,Sq,D] of out_dtype (QFA_BF16, QFA_FP16 or QFA_FP32), strides
+ *           (o_sb, o_sh, o_ss); base and row strides 16-byte aligned.
+ * lse:      nullable fp32 [B,H,Sq] contiguous output; non-NULL requests it.
+ * D must be 64 or 128.
+ */
+int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                 const int8_t* q8, const float* qs, const float* qmu,
+                 const int8_t* k8, const float* ks,
+                 const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                 float sm_scale,
+                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                 const int32_t* index, const int32_t* count, const int32_t* vbs,
+                 const float* v_scale, int nseg, const int64_t* seg,
+                 void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                 float* lse, void* stream);
+
+/*
+ * qfa_lse_merge — exact merge of two partial softmaxes over disjoint key sets
+ * (comfy-kitchen issue #177, Question 2; FlyDSL PR #886, split-K combine):
+ *   m = max(La, Lb); m = -inf -> O = 0, L = -inf;
+ *   else wa = exp(La - m), wb = exp(Lb - m),
+ *        O = (wa*Oa + wb*Ob) / (wa + wb), L = m + log(wa + wb).
+ * Arithmetic is fp32.
+ *
+ * o_a, o_b, o: [B,H,S,D] of their dtypes (QFA_BF16, QFA_FP16, QFA_FP32) with
+ *              their own strides; o may alias o_a or o_b exactly (same
+ *              pointer, dtype and strides). Bases and row strides 16-byte
+ *              aligned.
+ * lse_a, lse_b: fp32 [B,H,S] contiguous. lse: nullable fp32 [B,H,S] output,
+ *              may alias lse_a or lse_b.
+ * D must be 64 or 128.
+ */
+int qfa_lse_merge(int64_t B, int64_t H, int64_t S, int64_t D,
+                  const void* o_a, int a_dtype, int64_t a_sb, int64_t a_sh, int64_t a_ss, const float* lse_a,
+                  const void* o_b, int b_dtype, int64_t b_sb, int64_t b_sh, int64_t b_ss, const float* lse_b,
+                  void* o, int o_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss, float* lse,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QFA_H */

@@ -1,0 +1,209 @@
+"""INT8-QK / BF16-PV flash attention forward for AMD Instinct MI355X (gfx950).
+
+Thin PyTorch binding of libqfa.so: every function below marshals tensors
+into the C ABI of include/qfa.h (pointers, sizes, strides and the current
+HIP stream) and allocates outputs with torch when the caller passes none.
+All arithmetic runs in the library's HIP kernels; there is no fallback path.
+
+Functions (same names as the C entry points without the ``qfa_`` prefix):
+  quantize_qk(q, k, vbs=None, center_k=True)      -> dict of int8 codes and scales
+  blockmask_to_index(mask)                         -> (index, count)
+  attn_fwd(qk, v, ...)                             -> out or (out, lse)
+  lse_merge(o_a, lse_a, o_b, lse_b)                -> (out, lse)
+plus ``int8_attention``, the quantize + attend convenience call.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import QFA_BF16, QFA_FP16, QFA_FP32, QFAError
+
+__all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
+           "quantize_workspace_bytes"]
+
+_DT = {torch.bfloat16: QFA_BF16, torch.float16: QFA_FP16, torch.float32: QFA_FP32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _view(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B,H,S,D], got {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a unit channel stride")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name} dtype {t.dtype} is not supported")
+    return _DT[t.dtype], t.stride(0), t.stride(1), t.stride(2)
+
+
+def _no_grad(*ts):
+    if torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in ts):
+        raise ValueError("INT8-QK attention is inference-only (inputs require grad)")
+
+
+def _cont(t: torch.Tensor | None, name: str, dtype: torch.dtype):
+    if t is None:
+        return None
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+    return t
+
+
+def quantize_workspace_bytes(B: int, H: int, Sk: int, D: int) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.lib().qfa_quantize_workspace_bytes(B, H, Sk, D, ctypes.byref(n)))
+    return n.value
+
+
+def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = None, center_k: bool = True,
+                workspace: torch.Tensor | None = None) -> dict:
+    """Per-token symmetric int8 Q/K (+ K mean, centring term) on the GPU.
+
+    Returns dict(q8, qs, k8, ks, kmean, qmu); kmean/qmu are None when center_k is False.
+    """
+    _no_grad(q, k)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or k.dtype != q.dtype:
+        raise ValueError("q and k must agree in B, H, D and dtype")
+    dq, *qst = _view(q, "q")
+    _, *kst = _view(k, "k")
+    dev = q.device
+    vbs = _cont(vbs, "vbs", torch.int32)
+    q8 = torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev)
+    k8 = torch.empty((B, H, Sk, D), dtype=torch.int8, device=dev)
+    qs = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, H, Sk), dtype=torch.float32, device=dev)
+    kmean = torch.empty((B, H, D), dtype=torch.float32, device=dev) if center_k else None
+    qmu = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if center_k else None
+    nbytes = quantize_workspace_bytes(B, H, Sk, D) if center_k else 0
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _lib.check(_lib.lib().qfa_quantize_qk(
+        B, H, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
+        _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(kmean), _ptr(qmu),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev)))
+    return dict(q8=q8, qs=qs, k8=k8, ks=ks, kmean=kmean, qmu=qmu)
+
+
+def blockmask_to_index(mask: torch.Tensor):
+    """[B,H,Tq,Tk] bool/uint8 tile mask -> (index int32 [B,H,Tq,Tk], count int32 [B,H,Tq])."""
+    if mask.dim() != 4:
+        raise ValueError("mask must be [B,H,Tq,Tk]")
+    m = mask.contiguous()
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise ValueError("mask must be bool or uint8")
+    B, H, Tq, Tk = m.shape
+    index = torch.empty((B, H, Tq, Tk), dtype=torch.int32, device=m.device)
+    count = torch.empty((B, H, Tq), dtype=torch.int32, device=m.device)
+    _lib.check(_lib.lib().qfa_blockmask_to_index(_ptr(m), B, H, Tq, Tk, _ptr(index), _ptr(count),
+                                                 _stream(m.device)))
+    return index, count
+
+
+def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,
+             index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
+             v_scale: torch.Tensor | None = None, segments=None, out: torch.Tensor | None = None,
+             out_dtype: torch.dtype | None = None, return_lse: bool = False, lse: torch.Tensor | None = None):
+    """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
+
+    bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
+        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16.
+    index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
+    segments: up to 4 ascending disjoint (start, length) key ranges.
+    return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
+    """
+    _no_grad(v, bias)
+    q8, qs, k8, ks, qmu = qk["q8"], qk["qs"], qk["k8"], qk["ks"], qk.get("qmu")
+    B, H, Sq, D = q8.shape
+    Sk = k8.shape[2]
+    if v.shape != (B, H, Sk, D):
+        raise ValueError(f"v shape {tuple(v.shape)} != {(B, H, Sk, D)}")
+    _cont(q8, "q8", torch.int8), _cont(k8, "k8", torch.int8)
+    _cont(qs, "qs", torch.float32), _cont(ks, "ks", torch.float32), _cont(qmu, "qmu", torch.float32)
+    dv, *vst = _view(v, "v")
+    dev = v.device
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype or v.dtype, device=dev)
+    do, *ost = _view(out, "out")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    _cont(lse, "lse", torch.float32)
+    bptr, bdt, bsb, bsh = None, QFA_FP32, 0, 0
+    if bias is not None:
+        if bias.dim() != 4 or bias.shape[-1] != Sk or bias.stride(-1) != 1:
+            raise ValueError("bias must be [B|1,H|1,Q|1,K] with a unit key stride")
+        if bias.shape[-2] != 1 and bias.stride(-2) != 0:
+            raise NotImplementedError("a materialised per-query bias is not supported; pass [..,1,K] or a stride-0 expansion")
+        if bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H):
+            raise ValueError("bias batch/head dims must be 1 or match")
+        bdt = _DT.get(bias.dtype)
+        if bdt is None:
+            raise ValueError(f"bias dtype {bias.dtype}")
+        bsb = bias.stride(0) if bias.shape[0] > 1 else 0
+        bsh = bias.stride(1) if bias.shape[1] > 1 else 0
+        bptr = _ptr(bias)
+    _cont(index, "index", torch.int32), _cont(count, "count", torch.int32), _cont(vbs, "vbs", torch.int32)
+    _cont(v_scale, "v_scale", torch.float32)
+    nseg, seg = 0, None
+    if segments is not None:
+        segs = [int(x) for pair in segments for x in pair]
+        nseg = len(segs) // 2
+        seg = (ctypes.c_int64 * max(1, len(segs)))(*segs)
+    _lib.check(_lib.lib().qfa_attn_fwd(
+        B, H, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
+        _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
+        bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
+        _ptr(out), do, *ost, _ptr(lse), _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+              out: torch.Tensor | None = None, lse_out: torch.Tensor | None = None, out_dtype=None):
+    """Exact merge of two partial attentions over disjoint key sets -> (out, lse)."""
+    B, H, S, D = o_a.shape
+    if o_b.shape != o_a.shape or lse_a.shape != (B, H, S) or lse_b.shape != (B, H, S):
+        raise ValueError("partials must share [B,H,S,D] and lse [B,H,S]")
+    da, *ast = _view(o_a, "o_a")
+    db, *bst = _view(o_b, "o_b")
+    _cont(lse_a, "lse_a", torch.float32), _cont(lse_b, "lse_b", torch.float32)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=out_dtype or o_a.dtype, device=o_a.device)
+    do, *ost = _view(out, "out")
+    if lse_out is None:
+        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=o_a.device)
+    _cont(lse_out, "lse_out", torch.float32)
+    _lib.check(_lib.lib().qfa_lse_merge(B, H, S, D, _ptr(o_a), da, *ast, _ptr(lse_a), _ptr(o_b), db, *bst,
+                                        _ptr(lse_b), _ptr(out), do, *ost, _ptr(lse_out), _stream(o_a.device)))
+    return out, lse_out
+
+
+def int8_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                   attn_mask: torch.Tensor | None = None, *, return_lse: bool = False, center_k: bool = True,
+                   segments=None):
+    """Quantize Q/K once and attend (the comfy-kitchen-style entry point).
+
+    attn_mask: a per-key additive float bias [B|1,H|1,1|Q,K] (stride-0 over Q).
+    """
+    qk = quantize_qk(q, k, center_k=center_k)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return attn_fwd(qk, v, scale, bias=attn_mask, segments=segments, return_lse=return_lse)
+
+
+def sm_scale_default(D: int) -> float:
+    return float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))

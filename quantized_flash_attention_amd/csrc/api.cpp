@@ -1,0 +1,249 @@
+// C ABI of libqfa.so: argument checking, dispatch and launches on the
+// caller's stream. Every check runs before any launch, so a call that fails
+// leaves device memory untouched. The declarations and their documentation
+// are in include/qfa.h.
+#include "../../include/qfa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "qfa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return QFA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dt) { return dt == QFA_FP32 ? 4 : 2; }
+
+// A [B,H,S,D] tensor view: non-null, 16-byte aligned base, row strides whose
+// byte size is a multiple of 16 (D is 64 or 128 here, so a row is a whole
+// number of 16-byte chunks), non-negative strides.
+int check_view(const char* name, const void* p, int dt, int64_t sb, int64_t sh, int64_t ss) {
+  if (!p) return fail(QFA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(QFA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  if (sb < 0 || sh < 0 || ss < 0) return fail(QFA_ERR_INVALID_ARG, "%s has a negative stride", name);
+  const int64_t eb = elem_bytes(dt);
+  if ((sb * eb) % 16 || (sh * eb) % 16 || (ss * eb) % 16)
+    return fail(QFA_ERR_INVALID_ARG, "%s strides (%lld,%lld,%lld) are not multiples of 16 bytes", name,
+                (long long)sb, (long long)sh, (long long)ss);
+  return QFA_OK;
+}
+
+int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
+  if (D != 64 && D != 128) return fail(QFA_ERR_UNSUPPORTED, "head dimension %lld (supported: 64, 128)", (long long)D);
+  if (B * H > (1ll << 24) || Sq > (1ll << 30) || Sk > (1ll << 30))
+    return fail(QFA_ERR_UNSUPPORTED, "sizes beyond this build's 32-bit tile indexing");
+  return QFA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qfa_version(void) { return 100; }
+
+const char* qfa_status_string(int status) {
+  switch (status) {
+    case QFA_OK: return "ok";
+    case QFA_ERR_INVALID_ARG: return "invalid argument";
+    case QFA_ERR_UNSUPPORTED: return "unsupported";
+    case QFA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* qfa_last_error(void) { return g_err; }
+
+int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, size_t* bytes) {
+  if (!bytes) return fail(QFA_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0 || H < 0 || Sk < 0 || D <= 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
+  const int64_t nchunks = (Sk + qfa::kMeanChunkRows - 1) / qfa::kMeanChunkRows;
+  *bytes = (size_t)(B * H * nchunks * D) * 16;
+  return ok();
+}
+
+int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                    const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                    const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                    const int32_t* vbs, int center_k,
+                    int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if (dtype != QFA_BF16 && dtype != QFA_FP16)
+    return fail(dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "Q/K dtype %d (supported: bf16, fp16)", dtype);
+  if (B * H == 0) return ok();  // nothing to read or write: empty tensors may have NULL data
+  if (Sq > 0) {
+    if ((st = check_view("q", q, dtype, q_sb, q_sh, q_ss))) return st;
+    if (!q8 || !qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs output is NULL");
+    if (!aligned16(q8) || !aligned16(qs)) return fail(QFA_ERR_INVALID_ARG, "q8/qs outputs must be 16-byte aligned");
+  }
+  if (Sk > 0) {
+    if ((st = check_view("k", k, dtype, k_sb, k_sh, k_ss))) return st;
+    if (!k8 || !ks) return fail(QFA_ERR_INVALID_ARG, "k8/ks output is NULL");
+    if (!aligned16(k8) || !aligned16(ks)) return fail(QFA_ERR_INVALID_ARG, "k8/ks outputs must be 16-byte aligned");
+  }
+  if (vbs && (Sq != Sk || Sk % 64)) return fail(QFA_ERR_INVALID_ARG, "vbs requires Sq == Sk, a multiple of 64");
+  if (center_k) {
+    if (!kmean) return fail(QFA_ERR_INVALID_ARG, "kmean output is NULL with center_k");
+    if (!aligned16(kmean) || (qmu && !aligned16(qmu))) return fail(QFA_ERR_INVALID_ARG, "kmean/qmu must be 16-byte aligned");
+    size_t need = 0;
+    qfa_quantize_workspace_bytes(B, H, Sk, D, &need);
+    if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+      return fail(QFA_ERR_INVALID_ARG, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (center_k && Sk > 0) {
+    qfa::MeanArgs m{k, dtype, B, H, Sk, D, k_sb, k_sh, k_ss, vbs, (double2*)workspace, kmean,
+                    (int)((Sk + qfa::kMeanChunkRows - 1) / qfa::kMeanChunkRows)};
+    if ((st = hip_status(qfa::launch_kmean(m, s), "kmean launch"))) return st;
+  } else if (center_k) {
+    if ((st = hip_status(qfa::launch_zero_words(kmean, B * H * D, s), "kmean clear"))) return st;
+  }
+  if (Sq > 0) {
+    qfa::QuantRowsArgs qa{q, dtype, B, H, Sq, D, q_sb, q_sh, q_ss, nullptr,
+                          center_k ? kmean : nullptr, vbs, q8, qs, center_k ? qmu : nullptr};
+    if ((st = hip_status(qfa::launch_quantize_rows(qa, s), "quantize Q launch"))) return st;
+  }
+  if (Sk > 0) {
+    qfa::QuantRowsArgs ka{k, dtype, B, H, Sk, D, k_sb, k_sh, k_ss, center_k ? kmean : nullptr,
+                          nullptr, vbs, k8, ks, nullptr};
+    if ((st = hip_status(qfa::launch_quantize_rows(ka, s), "quantize K launch"))) return st;
+  }
+  return ok();
+}
+
+int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
+                           int32_t* index, int32_t* count, void* stream) {
+  if (B < 0 || H < 0 || Tq < 0 || Tk < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
+  if (B * H * Tq * Tk == 0) {
+    if (B * H * Tq > 0 && count) {
+      return hip_status(qfa::launch_zero_words(count, B * H * Tq, (hipStream_t)stream), "count clear");
+    }
+    return ok();
+  }
+  if (!mask || !index || !count) return fail(QFA_ERR_INVALID_ARG, "mask/index/count is NULL");
+  if (Tk > (1ll << 30)) return fail(QFA_ERR_UNSUPPORTED, "Tk too large");
+  return hip_status(qfa::launch_blockmask_to_index(mask, B * H * Tq, Tk, index, count, (hipStream_t)stream),
+                    "blockmask_to_index launch");
+}
+
+int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                 const int8_t* q8, const float* qs, const float* qmu,
+                 const int8_t* k8, const float* ks,
+                 const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                 float sm_scale,
+                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                 const int32_t* index, const int32_t* count, const int32_t* vbs,
+                 const float* v_scale, int nseg, const int64_t* seg,
+                 void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                 float* lse, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if (v_dtype != QFA_BF16 && v_dtype != QFA_FP16)
+    return fail(v_dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "V dtype %d (supported: bf16, fp16)", v_dtype);
+  if (B * H * Sq == 0) return ok();  // no output rows: empty tensors may have NULL data
+  if (!q8 || !qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs is NULL");
+  if (!aligned16(q8)) return fail(QFA_ERR_INVALID_ARG, "q8 must be 16-byte aligned");
+  if (Sk > 0) {  // with no keys every row is fully masked and K/V are never read
+    if (!k8 || !ks) return fail(QFA_ERR_INVALID_ARG, "k8/ks is NULL");
+    if (!aligned16(k8)) return fail(QFA_ERR_INVALID_ARG, "k8 must be 16-byte aligned");
+    if ((st = check_view("v", v, v_dtype, v_sb, v_sh, v_ss))) return st;
+  }
+  if (out_dtype != QFA_BF16 && out_dtype != QFA_FP16 && out_dtype != QFA_FP32)
+    return fail(QFA_ERR_INVALID_ARG, "out dtype %d", out_dtype);
+  if ((st = check_view("out", out, out_dtype, o_sb, o_sh, o_ss))) return st;
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(QFA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (v_scale && !aligned16(v_scale)) return fail(QFA_ERR_INVALID_ARG, "v_scale must be 16-byte aligned");
+  if (bias) {
+    if (bias_dtype != QFA_FP32 && bias_dtype != QFA_BF16 && bias_dtype != QFA_FP16)
+      return fail(QFA_ERR_INVALID_ARG, "bias dtype %d", bias_dtype);
+    if (bias_sb < 0 || bias_sh < 0) return fail(QFA_ERR_INVALID_ARG, "negative bias stride");
+    if (index) return fail(QFA_ERR_INVALID_ARG, "bias and block-sparse mask are mutually exclusive");
+  }
+  qfa::AttnArgs a{};
+  if (index) {
+    if (!count) return fail(QFA_ERR_INVALID_ARG, "block-sparse call without count");
+    if (Sq != Sk || Sk % 64) return fail(QFA_ERR_INVALID_ARG, "block-sparse needs Sq == Sk, a multiple of 64");
+    if (nseg != 0) return fail(QFA_ERR_INVALID_ARG, "segments are not combinable with a block-sparse mask");
+  }
+  if (nseg < 0 || nseg > QFA_MAX_SEGMENTS) return fail(QFA_ERR_INVALID_ARG, "nseg %d (0..4)", nseg);
+  if (nseg > 0 && !seg) return fail(QFA_ERR_INVALID_ARG, "seg is NULL with nseg > 0");
+  int64_t prev_end = 0;
+  for (int g = 0; g < nseg; ++g) {
+    const int64_t s0 = seg[2 * g], n = seg[2 * g + 1];
+    if (s0 < 0 || n < 0 || s0 + n > Sk)
+      return fail(QFA_ERR_INVALID_ARG, "segment %d [%lld, +%lld) outside [0, %lld)", g, (long long)s0, (long long)n, (long long)Sk);
+    if (s0 < prev_end) return fail(QFA_ERR_INVALID_ARG, "segments must be ascending and disjoint");
+    prev_end = s0 + n;
+    a.seg_lo[g] = (int)s0;
+    a.seg_hi[g] = (int)(s0 + n);
+  }
+  if (nseg == 0) {
+    a.seg_lo[0] = 0;
+    a.seg_hi[0] = (int)Sk;
+    nseg = 1;
+  }
+  a.nseg = nseg;
+  a.B = (int)B; a.H = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
+  a.q8 = q8; a.qs = qs; a.qmu = qmu; a.k8 = k8; a.ks = ks;
+  a.v = v; a.v_dtype = v_dtype; a.v_sb = v_sb; a.v_sh = v_sh; a.v_ss = v_ss;
+  a.sm_scale = sm_scale;
+  a.bias = bias; a.bias_dtype = bias_dtype; a.bias_sb = bias_sb; a.bias_sh = bias_sh;
+  a.index = index; a.count = count; a.vbs = index ? vbs : nullptr;
+  a.v_scale = v_scale;
+  a.out = out; a.out_dtype = out_dtype; a.o_sb = o_sb; a.o_sh = o_sh; a.o_ss = o_ss;
+  a.lse = lse;
+  return hip_status(qfa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+}
+
+int qfa_lse_merge(int64_t B, int64_t H, int64_t S, int64_t D,
+                  const void* o_a, int a_dtype, int64_t a_sb, int64_t a_sh, int64_t a_ss, const float* lse_a,
+                  const void* o_b, int b_dtype, int64_t b_sb, int64_t b_sh, int64_t b_ss, const float* lse_b,
+                  void* o, int o_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss, float* lse,
+                  void* stream) {
+  int st;
+  if ((st = check_dims(B, H, S, S, D))) return st;
+  for (int dt : {a_dtype, b_dtype, o_dtype})
+    if (dt != QFA_BF16 && dt != QFA_FP16 && dt != QFA_FP32) return fail(QFA_ERR_INVALID_ARG, "dtype %d", dt);
+  if (B * H * S == 0) return ok();
+  if ((st = check_view("o_a", o_a, a_dtype, a_sb, a_sh, a_ss))) return st;
+  if ((st = check_view("o_b", o_b, b_dtype, b_sb, b_sh, b_ss))) return st;
+  if ((st = check_view("o", o, o_dtype, o_sb, o_sh, o_ss))) return st;
+  if (!lse_a || !lse_b) return fail(QFA_ERR_INVALID_ARG, "lse_a/lse_b is NULL");
+  auto same = [&](const void* p, int dt, int64_t sb, int64_t sh, int64_t ss) {
+    return p == o && dt == o_dtype && sb == o_sb && sh == o_sh && ss == o_ss;
+  };
+  // o may alias an input only exactly (element-wise in place)
+  if (o == o_a && !same(o_a, a_dtype, a_sb, a_sh, a_ss)) return fail(QFA_ERR_INVALID_ARG, "o aliases o_a with another layout");
+  if (o == o_b && !same(o_b, b_dtype, b_sb, b_sh, b_ss)) return fail(QFA_ERR_INVALID_ARG, "o aliases o_b with another layout");
+  qfa::MergeArgs m{B, H, S, D, o_a, a_dtype, a_sb, a_sh, a_ss, lse_a, o_b, b_dtype, b_sb, b_sh, b_ss, lse_b,
+                   o, o_dtype, o_sb, o_sh, o_ss, lse};
+  return hip_status(qfa::launch_lse_merge(m, (hipStream_t)stream), "lse_merge launch");
+}
+
+}  // extern "C"

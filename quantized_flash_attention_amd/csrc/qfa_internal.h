@@ -1,0 +1,119 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950 kernels.
+// Argument checking happens in api.cpp; the launchers below trust their input.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qfa {
+
+enum DType : int { BF16 = 1, FP16 = 2, FP32 = 3 };
+
+// K mean: partial sums per (bh, chunk) in double-double, then one finalize.
+constexpr int kMeanChunkRows = 256;
+
+struct MeanArgs {
+  const void* k;
+  int dtype;
+  int64_t B, H, S, D;
+  int64_t sb, sh, ss;
+  const int32_t* vbs;   // nullable
+  double2* partial;     // [B*H, nchunks, D] (hi, lo)
+  float* mean;          // [B*H, D]
+  int nchunks;
+};
+hipError_t launch_kmean(const MeanArgs& a, hipStream_t s);
+
+struct QuantRowsArgs {
+  const void* x;
+  int dtype;
+  int64_t B, H, S, D;
+  int64_t sb, sh, ss;
+  const float* mean;    // nullable: centre rows by mean[bh, :]
+  const float* qmu_mean;// nullable: compute qmu = x . qmu_mean[bh, :] into qmu
+  const int32_t* vbs;   // nullable
+  int8_t* codes;        // [B*H*S, D]
+  float* scale;         // [B*H*S]
+  float* qmu;           // nullable [B*H*S]
+};
+hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+
+// Clears `words` 32-bit words with a fill kernel (never a memset node, so a
+// captured graph replays it faithfully).
+hipError_t launch_zero_words(void* p, int64_t words, hipStream_t s);
+
+hipError_t launch_blockmask_to_index(const uint8_t* mask, int64_t rows, int64_t Tk, int32_t* index,
+                                     int32_t* count, hipStream_t s);
+
+struct AttnArgs {
+  int B, H, Sq, Sk, D;
+  const int8_t* q8;
+  const float* qs;
+  const float* qmu;     // nullable
+  const int8_t* k8;
+  const float* ks;
+  const void* v;
+  int v_dtype;
+  int64_t v_sb, v_sh, v_ss;
+  float sm_scale;
+  const void* bias;     // nullable
+  int bias_dtype;
+  int64_t bias_sb, bias_sh;
+  const int32_t* index; // nullable (dense)
+  const int32_t* count;
+  const int32_t* vbs;   // nullable
+  const float* v_scale; // nullable [H, D]
+  int nseg;
+  int seg_lo[4], seg_hi[4];
+  void* out;
+  int out_dtype;
+  int64_t o_sb, o_sh, o_ss;
+  float* lse;           // nullable
+};
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+
+struct MergeArgs {
+  int64_t B, H, S, D;
+  const void* oa; int a_dtype; int64_t a_sb, a_sh, a_ss; const float* la;
+  const void* ob; int b_dtype; int64_t b_sb, b_sh, b_ss; const float* lb;
+  void* o; int o_dtype; int64_t o_sb, o_sh, o_ss; float* l;
+};
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+
+// ---- device helpers ----------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)x;
+}
+
+// Unpack 8 16-bit values held in a 16-byte word.
+template <int DT>
+__device__ __forceinline__ void unpack8(const uint4 w, float* f) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (DT == BF16) {
+      f[2 * i] = bf16_bits_to_float(u[i] & 0xffffu);
+      f[2 * i + 1] = bf16_bits_to_float(u[i] >> 16);
+    } else {
+      f[2 * i] = half_bits_to_float(u[i] & 0xffffu);
+      f[2 * i + 1] = half_bits_to_float(u[i] >> 16);
+    }
+  }
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t float_to_half_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace qfa

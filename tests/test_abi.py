@@ -1,0 +1,132 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_flash_attention_amd as qfa
+from quantized_flash_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qfa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libqfa.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(qfa_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert set(syms) == set(_lib.EXPORTS)
+    L = _lib.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert L.qfa_version() >= 100
+    assert L.qfa_status_string(2) == b"unsupported"
+
+
+def test_workspace_size():
+    n = qfa.quantize_workspace_bytes(1, 56, 33600, 128)
+    assert n == 56 * ((33600 + 255) // 256) * 128 * 16
+    assert qfa.quantize_workspace_bytes(1, 1, 0, 64) == 0
+
+
+def _quant(**kw):
+    a = dict(B=1, H=2, Sq=128, Sk=128, D=128, dtype=1, q=FAKE, q_s=(32768, 16384, 128), k=FAKE,
+             k_s=(32768, 16384, 128), vbs=None, center=1, outs=[FAKE] * 6, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return _lib.lib().qfa_quantize_qk(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["dtype"], a["q"], *a["q_s"],
+                                      a["k"], *a["k_s"], a["vbs"], a["center"], *a["outs"], a["ws"], a["wsb"], None)
+
+
+def test_quantize_rejects_bad_arguments():
+    assert _quant(D=96) == _lib.QFA_ERR_UNSUPPORTED
+    assert b"head dimension" in _lib.lib().qfa_last_error()
+    assert _quant(dtype=3) == _lib.QFA_ERR_UNSUPPORTED
+    assert _quant(dtype=7) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(q=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(q=ctypes.c_void_p(0x10008)) == _lib.QFA_ERR_INVALID_ARG  # misaligned
+    assert _quant(q_s=(32768, 16384, 100)) == _lib.QFA_ERR_INVALID_ARG     # row stride not 16-byte
+    assert _quant(vbs=FAKE, Sq=100, Sk=100) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(ws=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(wsb=16) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(outs=[FAKE, FAKE, FAKE, FAKE, None, FAKE]) == _lib.QFA_ERR_INVALID_ARG  # kmean with center_k
+    assert _quant(B=-1) == _lib.QFA_ERR_INVALID_ARG
+
+
+def _attn(**kw):
+    a = dict(B=1, H=2, Sq=128, Sk=128, D=128, qk=[FAKE] * 5, v=FAKE, vdt=1, v_s=(32768, 16384, 128), scale=0.088,
+             bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None,
+             out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
+    a.update(kw)
+    return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
+                                   ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a["index"],
+                                   a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["out"], a["odt"],
+                                   *a["o_s"], a["lse"], None)
+
+
+def _segs(*pairs):
+    flat = [x for p in pairs for x in p]
+    return (ctypes.c_int64 * len(flat))(*flat)
+
+
+def test_attn_rejects_bad_arguments():
+    assert _attn(D=80) == _lib.QFA_ERR_UNSUPPORTED
+    assert _attn(vdt=3) == _lib.QFA_ERR_UNSUPPORTED
+    assert _attn(odt=9) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(qk=[None] + [FAKE] * 4) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(scale=0.0) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(scale=float("nan")) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(bias=FAKE, index=FAKE, count=FAKE) == _lib.QFA_ERR_INVALID_ARG
+    assert b"mutually exclusive" in _lib.lib().qfa_last_error()
+    assert _attn(bias=FAKE, bdt=5) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(index=FAKE) == _lib.QFA_ERR_INVALID_ARG                       # no count
+    assert _attn(index=FAKE, count=FAKE, Sq=128, Sk=192) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(index=FAKE, count=FAKE, nseg=1, seg=_segs((0, 64))) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(nseg=5, seg=_segs(*[(0, 1)] * 5)) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(nseg=1, seg=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(nseg=1, seg=_segs((100, 40))) == _lib.QFA_ERR_INVALID_ARG      # past Sk
+    assert _attn(nseg=2, seg=_segs((50, 10), (55, 10))) == _lib.QFA_ERR_INVALID_ARG  # overlapping
+    assert _attn(nseg=2, seg=_segs((60, 10), (0, 10))) == _lib.QFA_ERR_INVALID_ARG   # descending
+    assert _attn(out=ctypes.c_void_p(0x10004)) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(vsc=ctypes.c_void_p(0x10004)) == _lib.QFA_ERR_INVALID_ARG
+
+
+def test_merge_rejects_bad_arguments():
+    L = _lib.lib()
+    st = (32768, 16384, 128)
+
+    def m(oa=FAKE, adt=1, ob=FAKE, o=FAKE, odt=1, o_s=st, la=FAKE, D=128):
+        return L.qfa_lse_merge(1, 2, 128, D, oa, adt, *st, la, ob, 1, *st, FAKE, o, odt, *o_s, None, None)
+
+    assert m(D=32) == _lib.QFA_ERR_UNSUPPORTED
+    assert m(adt=4) == _lib.QFA_ERR_INVALID_ARG
+    assert m(la=None) == _lib.QFA_ERR_INVALID_ARG
+    assert m(o=FAKE, odt=3) == _lib.QFA_ERR_INVALID_ARG         # aliases o_a with another dtype
+    assert m(o=FAKE, o_s=(32768, 16384, 256)) == _lib.QFA_ERR_INVALID_ARG
+
+
+def test_blockmask_rejects_bad_arguments():
+    L = _lib.lib()
+    assert L.qfa_blockmask_to_index(None, 1, 1, 4, 4, FAKE, FAKE, None) == _lib.QFA_ERR_INVALID_ARG
+    assert L.qfa_blockmask_to_index(FAKE, 1, -1, 4, 4, FAKE, FAKE, None) == _lib.QFA_ERR_INVALID_ARG
+    assert L.qfa_blockmask_to_index(FAKE, 0, 1, 4, 4, FAKE, FAKE, None) == _lib.QFA_OK  # empty: nothing to do
+
+
+def test_python_binding_refuses_grad_and_bad_bias():
+    import torch
+    q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="inference-only"):
+        qfa.quantize_qk(q, q)
+    qk = dict(q8=torch.zeros(1, 1, 64, 128, dtype=torch.int8), qs=torch.zeros(1, 1, 64),
+              k8=torch.zeros(1, 1, 64, 128, dtype=torch.int8), ks=torch.zeros(1, 1, 64))
+    v = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(NotImplementedError, match="per-query bias"):
+        qfa.attn_fwd(qk, v, bias=torch.zeros(1, 1, 64, 64))

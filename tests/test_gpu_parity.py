@@ -1,0 +1,344 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Quantized codes, scales, K mean, tile-index lists: bit-exact. Attention
+output: max-abs <= 2e-2 and mean-abs <= 2e-3 (fp32); LSE <= 1e-3 absolute.
+Sizes span several 128-query and 64-key tiles plus ragged tails; the
+full-size workloads are checked on sampled rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import DEV, as_bshd, check_lse, check_o, down, sample_rows, up
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import quantized_flash_attention_amd as qfa
+
+
+def gpu_quant(q, k, vbs=None, center=True, bshd=False):
+    tq, tk = up(q), up(k)
+    if bshd:
+        tq, tk = as_bshd(tq), as_bshd(tk)
+    return qfa.quantize_qk(tq, tk, None if vbs is None else up(vbs), center_k=center)
+
+
+def assert_quant_equal(g, ref, center=True):
+    for name in ("q8", "qs", "k8", "ks") + (("kmean",) if center else ()):
+        a, b = down(g[name]), ref[name]
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            raise AssertionError(f"{name}: {len(bad)} mismatches, first at {bad[0].tolist()}: "
+                                 f"gpu {a[tuple(bad[0])]} oracle {b[tuple(bad[0])]}")
+    if center:
+        qm = down(g["qmu"]).astype(np.float64)
+        assert np.max(np.abs(qm - ref["qmu"])) <= 1e-4 * max(1.0, np.abs(ref["qmu"]).max())
+
+
+# ---------------------------------------------------------------- quantize --
+
+QUANT_CASES = {
+    "tiny": dict(w="tiny"),
+    "dense4k_ragged": dict(w="dense4k", H=3, Sq=1000, Sk=1111),
+    "d64_fp16": dict(w="d64", B=2, H=2, Sq=777, Sk=530),
+    "band_small": dict(w="band", H=2, Sq=300, Sk=2100),
+}
+
+
+@pytest.mark.parametrize("case", list(QUANT_CASES))
+@pytest.mark.parametrize("bshd", [False, True])
+def test_quantize_bit_exact(case, bshd):
+    c = dict(QUANT_CASES[case])
+    w = W.WORKLOADS[c.pop("w")]
+    q, k, _ = W.make_qkv(w, **c)
+    g = gpu_quant(q, k, bshd=bshd)
+    assert_quant_equal(g, oracle.quantize_qk(q, k))
+
+
+def test_quantize_uncentred_and_vbs():
+    w = W.WORKLOADS["sparse"]
+    q, k, _ = W.make_qkv(w, H=3, Sq=320, Sk=320)
+    g = gpu_quant(q, k, center=False)
+    assert_quant_equal(g, oracle.quantize_qk(q, k, center_k=False), center=False)
+    vbs = np.array([64, 0, 64, 30, 17], np.int32)
+    W.zero_pads(q, vbs), W.zero_pads(k, vbs)
+    assert_quant_equal(gpu_quant(q, k, vbs), oracle.quantize_qk(q, k, vbs))
+
+
+def test_quantize_special_rows():
+    # zero rows, a row below the smallest normal scale, exact ties, huge values
+    w = W.WORKLOADS["tiny"]
+    q, k, _ = W.make_qkv(w, Sq=64, Sk=64)
+    qf = W.to_f32(q)
+    qf[0, 0, 0] = 0
+    qf[0, 0, 1] = 1e-37
+    qf[0, 0, 2, :4] = [2.0, 1.0, 0.5, 0.0]
+    qf[0, 0, 2, 4:] = 0
+    qf[0, 1, 3] *= 1e30
+    q2 = W.f32_to_bf16_bits(qf)
+    k2 = np.broadcast_to(k[:, :, :1], k.shape).copy()  # constant K: centres to zero rows
+    g = gpu_quant(q2, k2)
+    ref = oracle.quantize_qk(q2, k2)
+    assert_quant_equal(g, ref)
+    assert np.all(ref["k8"] == 0)
+
+
+@pytest.mark.parametrize("name", ["dense4k", "d64", "band", "sparse"])
+def test_quantize_full_size(name):
+    w = W.WORKLOADS[name]
+    q, k, _ = W.make_qkv(w)
+    vbs = None
+    if name == "sparse":
+        vbs = W.sparse_vbs(w.Sk // 64, w.extras["last_valid"])
+        W.zero_pads(q, vbs), W.zero_pads(k, vbs)
+    g = gpu_quant(q, k, vbs)
+    assert_quant_equal(g, oracle.quantize_qk(q, k, vbs))
+
+
+# --------------------------------------------------------------- attention --
+
+def _attn_case(w, q, k, v, *, bias=None, segments=None, vsc=None, out_dtype=None, bshd=False, rows=None):
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    tv = up(v)
+    if bshd:
+        tv = as_bshd(tv)
+    out = None
+    if bshd:
+        B, H, Sq, D = q.shape
+        out = torch.empty((B, Sq, H, D), dtype=out_dtype or tv.dtype, device=DEV).transpose(1, 2)
+    o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=None if bias is None else up(bias), segments=segments,
+                        v_scale=None if vsc is None else up(vsc), out=out, out_dtype=out_dtype, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, segments=segments, v_scale=vsc, rows=rows)
+    return o, l, o_ref, l_ref
+
+
+ATTN_CASES = {
+    "tiny": dict(w="tiny"),
+    "tiny_bias_f32": dict(w="tiny", bias="fp32"),
+    "dense4k_ragged": dict(w="dense4k", H=2, Sq=333, Sk=1000),
+    "d64_fp16_ragged": dict(w="d64", B=2, H=2, Sq=300, Sk=517),
+    "band_bias_bf16": dict(w="band", H=2, Sq=256, Sk=2100, bias="bf16"),
+    "band_bias_fp16": dict(w="band", H=1, Sq=130, Sk=700, bias="fp16"),
+    "band_segments": dict(w="band", H=2, Sq=200, Sk=2100, bias="fp32", segments=[(3, 600), (700, 1), (1500, 599)]),
+    "vscale_fp32_out": dict(w="sparse", H=2, Sq=192, Sk=192, vscale=True, out_dtype=torch.float32),
+    "bshd_views": dict(w="tiny", bshd=True, bias="fp32"),
+}
+
+
+@pytest.mark.parametrize("case", list(ATTN_CASES))
+def test_attn_parity(case):
+    c = dict(ATTN_CASES[case])
+    w = W.WORKLOADS[c.pop("w")]
+    bias_dt = c.pop("bias", None)
+    segments = c.pop("segments", None)
+    vscale = c.pop("vscale", False)
+    out_dtype = c.pop("out_dtype", None)
+    bshd = c.pop("bshd", False)
+    q, k, v = W.make_qkv(w, **c)
+    Sk = k.shape[2]
+    bias = None
+    if bias_dt:
+        b64 = W.band_bias(Sk, core=(Sk // 5, Sk - 2 * (Sk // 5)), skirt=Sk // 5)
+        if bias_dt == "fp16":
+            bias = b64.astype(np.float16).reshape(1, 1, 1, -1)
+        else:
+            bias = W.bias_tensor(b64, bias_dt)
+    vsc = W.v_scale(w, H=q.shape[1]) if vscale else None
+    o, l, o_ref, l_ref = _attn_case(w, q, k, v, bias=bias, segments=segments, vsc=vsc, out_dtype=out_dtype,
+                                    bshd=bshd)
+    if out_dtype is not None:
+        assert o.dtype == out_dtype
+    check_o(o, o_ref, what=case)
+    check_lse(l, l_ref, what=case)
+
+
+def test_attn_edge_cases():
+    w = W.WORKLOADS["tiny"]
+    # one key: O = V_0 (times nothing), LSE = the key's logit
+    q, k, v = W.make_qkv(w, Sq=70, Sk=1)
+    o, l, o_ref, l_ref = _attn_case(w, q, k, v)
+    check_o(o, o_ref, what="Sk=1")
+    check_lse(l, l_ref, what="Sk=1")
+    # every key masked by a -inf bias, and an empty segment: O = 0, LSE = -inf
+    q, k, v = W.make_qkv(w, Sq=40, Sk=100)
+    bias = np.full((1, 1, 1, 100), -np.inf, np.float32)
+    bias[..., 50:60] = 0.0
+    bias_dead = np.full((1, 1, 1, 100), -np.inf, np.float32)
+    for b, seg in ((bias_dead, None), (None, [(10, 0)]), (bias, [(0, 30), (70, 30)])):
+        o, l, o_ref, l_ref = _attn_case(w, q, k, v, bias=b, segments=seg)
+        assert np.all(o.float().cpu().numpy() == 0) and torch.all(torch.isneginf(l))
+        check_lse(l, l_ref)
+    # zero query rows attend uniformly
+    q0 = np.zeros_like(q)
+    o, l, o_ref, l_ref = _attn_case(w, q0, k, v, bias=bias)
+    check_o(o, o_ref, what="zero q")
+    check_lse(l, l_ref, what="zero q")
+    # empty query set is a no-op
+    g = gpu_quant(q[:, :, :0], k)
+    out = qfa.attn_fwd(g, up(v), w.sm_scale)
+    assert out.shape[2] == 0
+
+
+def test_attn_deterministic():
+    w = W.WORKLOADS["dense4k"]
+    q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
+    g = gpu_quant(q, k)
+    tv = up(v)
+    o1, l1 = qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True)
+    o2, l2 = qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_merge_small():
+    w = W.WORKLOADS["band"]
+    q, k, v = W.make_qkv(w, H=2, Sq=256, Sk=1680)
+    core, skirt = (336, 1008), 336
+    bias = W.bias_tensor(W.band_bias(1680, core=core, skirt=skirt), "fp32")
+    ref = oracle.quantize_qk(q, k)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias)
+    g = gpu_quant(q, k)
+    tv, tb = up(v), up(bias)
+    o_c, l_c = qfa.attn_fwd(g, tv, w.sm_scale, segments=[core], out_dtype=torch.float32, return_lse=True)
+    o_s, l_s = qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, segments=[(0, skirt), (core[0] + core[1], skirt)],
+                            out_dtype=torch.float32, return_lse=True)
+    o_m, l_m = qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+    check_o(o_m, o_ref, what="split+merge")
+    check_lse(l_m, l_ref, what="split+merge")
+    # the merge kernel itself against the oracle's merge of the same partials
+    mo, ml = oracle.lse_merge(o_c.cpu().numpy().reshape(-1, 128).astype(np.float64), l_c.cpu().numpy(),
+                              o_s.cpu().numpy().reshape(-1, 128).astype(np.float64), l_s.cpu().numpy())
+    o_m32, l_m32 = qfa.lse_merge(o_c, l_c, o_s, l_s)
+    assert np.max(np.abs(o_m32.cpu().numpy().reshape(-1, 128) - mo)) <= 1e-5
+    assert np.max(np.abs(l_m32.cpu().numpy().reshape(-1) - ml)) <= 1e-5
+    # in place into the first partial
+    qfa.lse_merge(o_c, l_c, o_s, l_s, out=o_c, lse_out=l_c)
+    assert torch.equal(o_c, o_m32) and torch.equal(l_c, l_m32)
+
+
+def test_merge_neg_inf_partials():
+    a = torch.randn(1, 2, 64, 64, device=DEV)
+    la = torch.randn(1, 2, 64, device=DEV)
+    dead = torch.full_like(la, -float("inf"))
+    o, l = qfa.lse_merge(a, la, torch.zeros_like(a), dead)
+    assert torch.allclose(o, a, atol=0, rtol=0) and torch.equal(l, la)
+    o, l = qfa.lse_merge(torch.zeros_like(a), dead, torch.zeros_like(a), dead)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+# ------------------------------------------------------------ block-sparse --
+
+def test_blockmask_to_index_exact():
+    rs = np.random.default_rng(21)
+    mask = rs.random((2, 3, 37, 200)) < 0.2
+    mask[0, 0, 0] = False
+    mask[1, 2, 3] = True
+    idx, cnt = qfa.blockmask_to_index(up(mask))
+    r_idx, r_cnt = oracle.blockmask_to_index(mask)
+    cnt = cnt.cpu().numpy()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(cnt, r_cnt)
+    for b, h, t in np.ndindex(2, 3, 37):
+        n = r_cnt[b, h, t]
+        assert np.array_equal(idx[b, h, t, :n], r_idx[b, h, t, :n])
+
+
+def _sparse_case(T, H, mask, vbs, rows=None):
+    w = W.WORKLOADS["sparse"]
+    S = 64 * T
+    q, k, v = W.make_qkv(w, H=H, Sq=S, Sk=S)
+    for x in (q, k, v):
+        W.zero_pads(x, vbs)
+    vsc = W.v_scale(w, H=H)
+    ref = oracle.quantize_qk(q, k, vbs)
+    g = gpu_quant(q, k, vbs)
+    assert_quant_equal(g, ref)
+    idx, cnt = qfa.blockmask_to_index(up(mask))
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, index=idx, count=cnt, vbs=up(vbs), v_scale=up(vsc), return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, mask=mask, vbs=vbs, v_scale=vsc, rows=rows)
+    return o, l, o_ref, l_ref
+
+
+def test_sparse_parity_small():
+    T, H = 9, 2
+    rs = np.random.default_rng(8)
+    mask = rs.random((1, H, T, T)) < 0.35
+    mask[0, 0, 4] = False          # a query tile with no key tile: O = 0, LSE = -inf
+    mask[0, 1, :, 0] = True
+    vbs = np.array([64, 64, 10, 64, 0, 64, 64, 33, 17], np.int32)
+    o, l, o_ref, l_ref = _sparse_case(T, H, mask, vbs)
+    check_o(o, o_ref, what="sparse")
+    check_lse(l, l_ref, what="sparse")
+
+
+def test_sparse_band_structure():
+    T, H = 40, 2
+    mask = W.sparse_mask(T, H, prefix=3, band=5)
+    vbs = W.sparse_vbs(T, 17)
+    o, l, o_ref, l_ref = _sparse_case(T, H, mask, vbs)
+    check_o(o, o_ref, what="sparse band")
+    check_lse(l, l_ref, what="sparse band")
+
+
+# --------------------------------------------------- full-size, sampled rows --
+
+def test_band_full_size_sampled():
+    """B1 H56 Sq4096 Sk33600 D128: unmasked, fp32 bias, bf16 bias and core+skirt split, as timed."""
+    w = W.WORKLOADS["band"]
+    q, k, v = W.make_qkv(w)
+    core, skirt = w.extras["core"], w.extras["skirt"]
+    b64 = W.band_bias(w.Sk, core=core, skirt=skirt)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    assert_quant_equal(g, ref)
+    tv = up(v)
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=24, heads=[0, 13, 55])
+    o, l = qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows)
+    check_o(o, o_ref, rows, "unmasked")
+    check_lse(l, l_ref, rows, "unmasked")
+    for dt in ("fp32", "bf16"):
+        bias = W.bias_tensor(b64, dt)
+        o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=up(bias), return_lse=True)
+        o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
+        check_o(o, o_ref, rows, f"bias {dt}")
+        check_lse(l, l_ref, rows, f"bias {dt}")
+    bias = W.bias_tensor(b64, "fp32")
+    tb = up(bias)
+    o_c, l_c = qfa.attn_fwd(g, tv, w.sm_scale, segments=[core], out_dtype=torch.float32, return_lse=True)
+    o_s, l_s = qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, segments=[(0, skirt), (core[0] + core[1], skirt)],
+                            out_dtype=torch.float32, return_lse=True)
+    o_m, l_m = qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
+    check_o(o_m, o_ref, rows, "split+merge")
+    check_lse(l_m, l_ref, rows, "split+merge")
+
+
+@pytest.mark.parametrize("name", ["dense4k", "d64"])
+def test_dense_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    q, k, v = W.make_qkv(w)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    assert_quant_equal(g, ref)
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=32)
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows)
+    check_o(o, o_ref, rows, name)
+    check_lse(l, l_ref, rows, name)
+
+
+def test_sparse_full_size_sampled():
+    """B1 H24 S131072 D128, prefix-8 + band-48 tile mask, vbs last tile 17, V scale."""
+    w = W.WORKLOADS["sparse"]
+    T = w.Sk // 64
+    mask = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
+    vbs = W.sparse_vbs(T, w.extras["last_valid"])
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=24, heads=[0, 23])
+    rows = np.unique(np.r_[rows, w.Sq - 1 - np.arange(64)])  # the ragged last tile incl. pad rows
+    o, l, o_ref, l_ref = _sparse_case(T, w.H, mask, vbs, rows=rows)
+    check_o(o, o_ref, rows, "sparse full")
+    check_lse(l, l_ref, rows, "sparse full")
