@@ -105,7 +105,9 @@ struct TileIter {
   }
 };
 
-template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS>
+// LSE is a compile-time trait: the LSE store exists only in the instances
+// that return it, so the plain kernels carry no runtime branch for it.
+template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
   constexpr int NT = NW * 64;
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       }
     }
   }
-  if (a.lse && hl == 0) {
+  if (LSE && hl == 0) {
     float L = -INFINITY;
     if (l_tot > 0.0f) {
       L = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -397,11 +399,14 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   const int total = qtiles * a.B * a.H;
   if (total == 0) return hipSuccess;
   if (sparse) {
-    attn_fwd_kernel<D, VT, 2, true, false><<<total, 128, 0, s>>>(a, qtiles, total);
+    if (a.lse) attn_fwd_kernel<D, VT, 2, true, false, true><<<total, 128, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 2, true, false, false><<<total, 128, 0, s>>>(a, qtiles, total);
   } else if (a.bias) {
-    attn_fwd_kernel<D, VT, 4, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);
   } else {
-    attn_fwd_kernel<D, VT, 4, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (a.lse) attn_fwd_kernel<D, VT, 4, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, false, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
   }
   return hipGetLastError();
 }
