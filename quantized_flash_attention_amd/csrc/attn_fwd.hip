@@ -44,6 +44,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -74,35 +76,79 @@ __device__ __forceinline__ float load_bias(const void* p, int dtype, int64_t idx
 }
 
 // Key-tile iteration: either the tiles covering up to 4 key segments, or the
-// key-tile list of this query tile (block-sparse).
+// key-tile list of this query tile (block-sparse). Every field is uniform
+// across the block; plain scalars (no arrays) keep them in SGPRs.
 struct TileIter {
-  int n;               // number of tiles
-  int seg_t0[4], seg_n[4], seg_lo[4], seg_hi[4];
-  int nseg;
-  const int32_t* list; // sparse: key tiles
-  const int32_t* vbs;  // sparse: valid counts (nullable)
-  int ntiles_k;        // sparse: number of key tiles
+  int n;                                  // number of tiles
+  int t0_0, t0_1, t0_2, t0_3;             // first tile of each segment
+  int n_0, n_1, n_2;                      // tiles of segments 0..2 (segment 3 takes the rest)
+  int lo_0, lo_1, lo_2, lo_3, hi_0, hi_1, hi_2, hi_3;
+  const int32_t* list;                    // sparse: key tiles
+  const int32_t* vbs;                     // sparse: valid counts (nullable)
+  int ntiles_k;                           // sparse: number of key tiles
 
   // tile index and the valid key range [lo, hi) inside it (absolute keys).
   // A listed tile outside [0, ntiles_k) is treated as an empty tile.
   __device__ __forceinline__ void get(int it, int& tile, int& lo, int& hi) const {
     if (list) {
-      tile = list[it];
+      tile = __builtin_amdgcn_readfirstlane(list[it]);
       if (tile < 0 || tile >= ntiles_k) {
         tile = 0;
         lo = hi = 0;
         return;
       }
       lo = tile * BN;
-      hi = lo + (vbs ? min(max(vbs[tile], 0), BN) : BN);
+      hi = lo + (vbs ? min(max(__builtin_amdgcn_readfirstlane(vbs[tile]), 0), BN) : BN);
       return;
     }
-    int g = 0;
-    while (g + 1 < nseg && it >= seg_n[g]) { it -= seg_n[g]; ++g; }
-    tile = seg_t0[g] + it;
-    lo = max(seg_lo[g], tile * BN);
-    hi = min(seg_hi[g], tile * BN + BN);
+    int t0, slo, shi;
+    if (it < n_0) {
+      t0 = t0_0; slo = lo_0; shi = hi_0;
+    } else if ((it -= n_0) < n_1) {
+      t0 = t0_1; slo = lo_1; shi = hi_1;
+    } else if ((it -= n_1) < n_2) {
+      t0 = t0_2; slo = lo_2; shi = hi_2;
+    } else {
+      it -= n_2;
+      t0 = t0_3; slo = lo_3; shi = hi_3;
+    }
+    tile = t0 + it;
+    lo = max(slo, tile * BN);
+    hi = min(shi, tile * BN + BN);
   }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// 16-byte load through a buffer resource; offsets at or past the resource's
+// size read as zero (hardware range check), so tile tails need no branches.
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+__device__ __forceinline__ float xmax32(float x) {
+  // max with the partner lane (lane ^ 32): v_permlane32_swap hands each lane
+  // the value of the other half-wave
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ float xsum32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int D>
+struct Smem {
+  unsigned char k[BN * Tile<D>::kStride];
+  unsigned char v[BN * Tile<D>::vStride];
+  float ks[BN];   // key scales
+  float lb[BN];   // log2-domain additive term per key: bias*log2(e), or -inf for an excluded key
 };
 
 // LSE is a compile-time trait: the LSE store exists only in the instances
@@ -118,11 +164,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   constexpr int V_PER_T = V_CHUNKS / NT;
   static_assert(K_CHUNKS % NT == 0 && V_CHUNKS % NT == 0, "tile split");
   using T = Tile<D>;
+  typedef typename std::conditional<VT == BF16, v8bf, v8h>::type pvec;
 
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[T::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[T::vBytes];
-  __shared__ __attribute__((aligned(16))) float ks_lds[BN];
-  __shared__ __attribute__((aligned(16))) float lb_lds[BN];
+  // two stages: tile i is computed from one while tile i+1 is written to the other
+  __shared__ __attribute__((aligned(16))) Smem<D> sm[2];
 
   const int bid = xcd_remap((int)blockIdx.x, total_blocks);
   const int bh = bid / qtiles, qt = bid % qtiles;
@@ -134,32 +179,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const int64_t qrow = (int64_t)bh * a.Sq + q;
 
   // ---- tile list ----
-  TileIter it;
-  it.list = nullptr;
-  it.vbs = nullptr;
-  it.nseg = 0;
-  it.ntiles_k = 0;
+  TileIter it{};
   if (SPARSE) {
     const int T = a.Sk / BN;
     it.list = a.index + ((int64_t)bh * T + qt) * T;
     it.vbs = a.vbs;
     it.ntiles_k = T;
-    it.n = min(max(a.count[(int64_t)bh * T + qt], 0), T);
+    it.n = min(max(__builtin_amdgcn_readfirstlane(a.count[(int64_t)bh * T + qt]), 0), T);
   } else {
-    it.nseg = a.nseg;
-    it.n = 0;
-    for (int g = 0; g < 4; ++g) {
-      if (g < a.nseg) {
-        const int t0 = a.seg_lo[g] / BN, t1 = (a.seg_hi[g] + BN - 1) / BN;
-        it.seg_t0[g] = t0;
-        it.seg_n[g] = a.seg_hi[g] > a.seg_lo[g] ? t1 - t0 : 0;
-        it.seg_lo[g] = a.seg_lo[g];
-        it.seg_hi[g] = a.seg_hi[g];
-        it.n += it.seg_n[g];
-      } else {
-        it.seg_t0[g] = it.seg_n[g] = it.seg_lo[g] = it.seg_hi[g] = 0;
-      }
-    }
+    // segments beyond nseg are empty; the host passes at least one
+    auto seg = [&](int g, int& t0, int& n, int& lo, int& hi) {
+      lo = g < a.nseg ? a.seg_lo[g] : 0;
+      hi = g < a.nseg ? a.seg_hi[g] : 0;
+      t0 = lo / BN;
+      n = hi > lo ? (hi + BN - 1) / BN - t0 : 0;
+    };
+    int n3;
+    seg(0, it.t0_0, it.n_0, it.lo_0, it.hi_0);
+    seg(1, it.t0_1, it.n_1, it.lo_1, it.hi_1);
+    seg(2, it.t0_2, it.n_2, it.lo_2, it.hi_2);
+    seg(3, it.t0_3, n3, it.lo_3, it.hi_3);
+    it.n = it.n_0 + it.n_1 + it.n_2 + n3;
   }
 
   // ---- Q codes for this lane's row: kept in VGPRs for the whole key loop ----
@@ -171,53 +211,60 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   }
   const float crow = qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f;
 
-  const int8_t* kbase = a.k8 + (int64_t)bh * a.Sk * D;
+  // ---- per-(b,h) sources; every tile load is a range-checked buffer load ----
+  const unsigned char* kbase = (const unsigned char*)(a.k8 + (int64_t)bh * a.Sk * D);
+  const int64_t k_bytes = (int64_t)a.Sk * D;
+  const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * 2;
+  const int64_t v_bytes = a.Sk > 0 ? ((int64_t)(a.Sk - 1) * a.v_ss + D) * 2 : 0;
+  const int v_row = (int)(a.v_ss * 2);
   const float* ksbase = a.ks + (int64_t)bh * a.Sk;
-  const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
+
+  // per-thread constant offsets inside a tile
+  int k_off[K_PER_T], v_off[V_PER_T], k_lds[K_PER_T], v_lds[V_PER_T];
+#pragma unroll
+  for (int i = 0; i < K_PER_T; ++i) {
+    const int c = tid + i * NT, row = c / (D / 16), col = c % (D / 16);
+    k_off[i] = row * D + col * 16;
+    k_lds[i] = row * T::kStride + col * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < V_PER_T; ++i) {
+    const int c = tid + i * NT, row = c / (D / 8), col = c % (D / 8);
+    v_off[i] = row * v_row + col * 16;
+    v_lds[i] = row * T::vStride + col * 16;
+  }
 
   // ---- staging registers for one tile ----
   uint4 kreg[K_PER_T], vreg[V_PER_T];
   float ksreg = 0.0f, lbreg = 0.0f;
 
-  auto gload = [&](int tile) {
-    const int key0 = tile * BN;
+  auto gload = [&](int tile, int lo, int hi) {
+    const int key0 = __builtin_amdgcn_readfirstlane(tile * BN);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * D, k_bytes - (int64_t)key0 * D);
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc(vbase + (int64_t)key0 * v_row, v_bytes - (int64_t)key0 * v_row);
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 16), col = c % (D / 16);
-      const int key = key0 + row;
-      kreg[i] = key < a.Sk ? *(const uint4*)(kbase + (int64_t)key * D + col * 16) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < K_PER_T; ++i) kreg[i] = bload16(kr, k_off[i]);
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int key = key0 + row;
-      vreg[i] = key < a.Sk ? *(const uint4*)(vbase + (int64_t)key * a.v_ss + col * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < V_PER_T; ++i) vreg[i] = bload16(vr, v_off[i]);
     if (tid < BN) {
       const int key = key0 + tid;
-      ksreg = key < a.Sk ? ksbase[key] : 0.0f;
-      if (HAS_BIAS) lbreg = key < a.Sk ? load_bias(a.bias, a.bias_dtype, bias_off + key) * kLog2e : 0.0f;
+      const bool in = key >= lo && key < hi;   // [lo, hi) lies inside [0, Sk)
+      ksreg = in ? ksbase[key] : 0.0f;
+      float lbv = 0.0f;
+      if (HAS_BIAS && in) lbv = load_bias(a.bias, a.bias_dtype, bias_off + key) * kLog2e;
+      lbreg = in ? lbv : -INFINITY;
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](Smem<D>& s) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 16), col = c % (D / 16);
-      *(uint4*)(k_lds + row * T::kStride + col * 16) = kreg[i];
-    }
+    for (int i = 0; i < K_PER_T; ++i) *(uint4*)(s.k + k_lds[i]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *(uint4*)(v_lds + row * T::vStride + col * 16) = vreg[i];
-    }
+    for (int i = 0; i < V_PER_T; ++i) *(uint4*)(s.v + v_lds[i]) = vreg[i];
     if (tid < BN) {
-      ks_lds[tid] = ksreg;
-      if (HAS_BIAS) lb_lds[tid] = lbreg;
+      s.ks[tid] = ksreg;
+      s.lb[tid] = lbreg;
     }
   };
 
@@ -225,7 +272,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   v16f o[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) o[c] = v16f{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;
+  float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // ds_read_b64_tr_b16 source addressing (per 16-lane group): lane s of the
   // group reads 4 channels at (key0 + s/4, dbase + 4*(s%4)); the hardware
@@ -237,18 +285,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   if (it.n > 0) {
     int tile, lo, hi;
     it.get(0, tile, lo, hi);
-    gload(tile);
-    lstore();
+    gload(tile, lo, hi);
+    lstore(sm[0]);
     __syncthreads();
   }
 
   for (int iter = 0; iter < it.n; ++iter) {
+    Smem<D>& cur = sm[iter & 1];
     int tile, lo, hi;
     it.get(iter, tile, lo, hi);
+    // unmasked tile without bias: scores need no additive term
+    const bool plain = !HAS_BIAS && lo == tile * BN && hi == tile * BN + BN;
     if (iter + 1 < it.n) {
       int t2, l2, h2;
       it.get(iter + 1, t2, l2, h2);
-      gload(t2);
+      gload(t2, l2, h2);
     }
 
     // ---- S^T = K8 Q8^T: two 32-key blocks ----
@@ -258,76 +309,85 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       s[blk] = v16i{};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const v4i kv = *(const v4i*)(k_lds + (32 * blk + (lane % 32)) * T::kStride + 32 * c + 16 * hl);
+        const v4i kv = *(const v4i*)(cur.k + (32 * blk + (lane % 32)) * T::kStride + 32 * c + 16 * hl);
         s[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qreg[c], s[blk], 0, 0, 0);
       }
     }
 
-    // ---- dequantize (+bias), mask, row max ----
-    const int klo = lo - tile * BN, khi = hi - tile * BN;  // valid keys within the tile
-    const bool full = (klo == 0 && khi == BN);
+    // ---- dequantize: u = S * ks (plain tiles keep u, the others take t = u*c + lb) ----
     float t[2][16];
-    float mx = -INFINITY;
+    float mx;
+    if (plain) {
+      float um = -INFINITY;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kk0 = 32 * blk + 8 * g + 4 * hl;
-        const float4 kv = *(const float4*)(ks_lds + kk0);
-        float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (HAS_BIAS) bv = *(const float4*)(lb_lds + kk0);
-        const float kvs[4] = {kv.x, kv.y, kv.z, kv.w};
-        const float bvs[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float u = (float)s[blk][4 * g + r] * kvs[r];
-          float x = HAS_BIAS ? fmaf(u, crow, bvs[r]) : u * crow;
-          if (!full) {
-            const int kk = kk0 + r;
-            x = (kk >= klo && kk < khi) ? x : -INFINITY;
-          }
-          t[blk][4 * g + r] = x;
-          mx = fmaxf(mx, x);
+        for (int g = 0; g < 4; ++g) {
+          const float4 kv = *(const float4*)(cur.ks + 32 * blk + 8 * g + 4 * hl);
+          t[blk][4 * g + 0] = (float)s[blk][4 * g + 0] * kv.x;
+          t[blk][4 * g + 1] = (float)s[blk][4 * g + 1] * kv.y;
+          t[blk][4 * g + 2] = (float)s[blk][4 * g + 2] * kv.z;
+          t[blk][4 * g + 3] = (float)s[blk][4 * g + 3] * kv.w;
+          um = max3(max3(um, t[blk][4 * g], t[blk][4 * g + 1]), t[blk][4 * g + 2], t[blk][4 * g + 3]);
         }
-      }
+      mx = xmax32(um) * crow;     // crow >= 0, so max(u)*c = max(u*c)
+    } else {
+      float tm = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 kv = *(const float4*)(cur.ks + 32 * blk + 8 * g + 4 * hl);
+          const float4 bv = *(const float4*)(cur.lb + 32 * blk + 8 * g + 4 * hl);
+          t[blk][4 * g + 0] = fmaf((float)s[blk][4 * g + 0] * kv.x, crow, bv.x);
+          t[blk][4 * g + 1] = fmaf((float)s[blk][4 * g + 1] * kv.y, crow, bv.y);
+          t[blk][4 * g + 2] = fmaf((float)s[blk][4 * g + 2] * kv.z, crow, bv.z);
+          t[blk][4 * g + 3] = fmaf((float)s[blk][4 * g + 3] * kv.w, crow, bv.w);
+          tm = max3(max3(tm, t[blk][4 * g], t[blk][4 * g + 1]), t[blk][4 * g + 2], t[blk][4 * g + 3]);
+        }
+      mx = xmax32(tm);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-    // ---- lazy rescale (wave-uniform branch) ----
-    const bool need = mx > m_run + kRescaleSlack;
-    if (__any(need)) {
+    // ---- lazy rescale: only when a row max passes the reference by the slack ----
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
 #pragma unroll
       for (int c = 0; c < KC; ++c) o[c] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    // plain tiles hold u and need t = u*c; the others already hold t
+    const float tscale = plain ? crow : 1.0f;
 
-    // ---- p = exp2(t - m), row sum (kept per lane), PV ----
+    // ---- p = exp2(t - m) as packed P^T operands, row sum on the packed values, PV ----
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(t[blk][r] - m_use);
-        t[blk][r] = p;
-        l_run += p;
-      }
-#pragma unroll
       for (int m = 0; m < 2; ++m) {
-        // B operand: P^T, keys 32*blk + 16*m + {0..3, 8..11} + 4*hl of this lane's row
-        typedef typename std::conditional<VT == BF16, v8bf, v8h>::type pvec;
-        pvec pb;
+        // the row sum takes the fp32 values: a sum of bf16-rounded p would
+        // carry up to 2^-9 relative error into the LSE when one key dominates
+        uint32_t pw[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (VT == BF16) pb[e] = (__bf16)t[blk][8 * m + e];
-          else pb[e] = (_Float16)t[blk][8 * m + e];
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(t[blk][8 * m + 2 * e], tscale, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(t[blk][8 * m + 2 * e + 1], tscale, -m_use));
+          lsum[e] += p0 + p1;
+          if constexpr (VT == BF16) {
+            const v2bf pair = {(__bf16)p0, (__bf16)p1};
+            pw[e] = __builtin_bit_cast(uint32_t, pair);
+          } else {
+            const v2h pair = {(_Float16)p0, (_Float16)p1};
+            pw[e] = __builtin_bit_cast(uint32_t, pair);
+          }
         }
+        const pvec pb = __builtin_bit_cast(pvec, pw);
         const int krow = 32 * blk + 16 * m + tr_row;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          const unsigned char* p0 = v_lds + krow * T::vStride + (32 * c + tr_col) * 2;
+          const unsigned char* p0 = cur.v + krow * T::vStride + (32 * c + tr_col) * 2;
           const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
           const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4s*)(p0 + 8 * T::vStride));
@@ -343,15 +403,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       }
     }
 
+    if (iter + 1 < it.n) lstore(sm[(iter + 1) & 1]);
     __syncthreads();
-    if (iter + 1 < it.n) {
-      lstore();
-      __syncthreads();
-    }
   }
 
   // ---- epilogue: O = O_acc / l * v_scale, LSE ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xsum32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
   if (!qvalid) return;
   const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int64_t obase = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)q * a.o_ss;
