@@ -69,6 +69,8 @@ def main() -> int:
     ap.add_argument("--variant-iters", type=int, default=20, help="iterations of each per-call timing loop")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of head 0 the oracle computes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -242,6 +244,14 @@ def main() -> int:
                          "step_tflops": round(page_value, 1)},
         "input_gen_s": round(gen_s, 1),
     }
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
 
     if args.cpu_baseline == "on":
         out["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, bias32_np, w, core, skirts, args.cpu_rows)

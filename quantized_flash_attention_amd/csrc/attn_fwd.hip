@@ -55,6 +55,14 @@ constexpr float kRescaleSlack = 8.0f;
 
 constexpr int BN = 64;  // keys per tile
 
+// The int32 score accumulators start at the bit pattern of 1.5*2^23, so the
+// MFMA leaves bits(1.5*2^23) + S: read as fp32 that is exactly 1.5*2^23 + S
+// (|S| <= 128*127^2 < 2^22). Then S*ks = fma(x, ks, -1.5*2^23*ks), one
+// instruction instead of a convert and a multiply; the rounding of the
+// per-key constant adds at most 0.75*ks (under one unit of S) to S*ks.
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
 template <int D>
 struct Tile {
   static constexpr int kStride = D + 16;        // bytes per K8 row in LDS
@@ -131,6 +139,20 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// max of 32 values as a tree of v_max3
+__device__ __forceinline__ float max32(const float (&t)[2][16]) {
+  float a[11];
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int i = 3 * k, j = 3 * k + 1, l = 3 * k + 2;
+    a[k] = max3(t[i / 16][i % 16], t[j / 16][j % 16], t[l / 16][l % 16]);
+  }
+  a[10] = fmaxf(t[1][14], t[1][15]);
+  const float b0 = max3(a[0], a[1], a[2]), b1 = max3(a[3], a[4], a[5]), b2 = max3(a[6], a[7], a[8]);
+  const float b3 = fmaxf(a[9], a[10]);
+  return fmaxf(max3(b0, b1, b2), b3);
+}
+
 __device__ __forceinline__ float xmax32(float x) {
   // max with the partner lane (lane ^ 32): v_permlane32_swap hands each lane
   // the value of the other half-wave
@@ -148,6 +170,7 @@ struct Smem {
   unsigned char k[BN * Tile<D>::kStride];
   unsigned char v[BN * Tile<D>::vStride];
   float ks[BN];   // key scales
+  float nks[BN];  // -kMagic * ks: turns the biased accumulator into S*ks with one FMA
   float lb[BN];   // log2-domain additive term per key: bias*log2(e), or -inf for an excluded key
 };
 
@@ -264,6 +287,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     for (int i = 0; i < V_PER_T; ++i) *(uint4*)(s.v + v_lds[i]) = vreg[i];
     if (tid < BN) {
       s.ks[tid] = ksreg;
+      s.nks[tid] = -kMagic * ksreg;
       s.lb[tid] = lbreg;
     }
   };
@@ -290,23 +314,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     __syncthreads();
   }
 
+  // one key tile per iteration: tile `iter` is in `cur`; tile iter+1 is
+  // fetched meanwhile and written to `nxt`
   for (int iter = 0; iter < it.n; ++iter) {
     Smem<D>& cur = sm[iter & 1];
+    Smem<D>& nxt = sm[(iter + 1) & 1];
     int tile, lo, hi;
     it.get(iter, tile, lo, hi);
     // unmasked tile without bias: scores need no additive term
     const bool plain = !HAS_BIAS && lo == tile * BN && hi == tile * BN + BN;
-    if (iter + 1 < it.n) {
+    const bool more = iter + 1 < it.n;
+    if (more) {
       int t2, l2, h2;
       it.get(iter + 1, t2, l2, h2);
       gload(t2, l2, h2);
     }
 
-    // ---- S^T = K8 Q8^T: two 32-key blocks ----
+    // ---- S^T = K8 Q8^T: two 32-key blocks, accumulators biased by kMagicBits ----
     v16i s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = v16i{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[blk][r] = kMagicBits;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const v4i kv = *(const v4i*)(cur.k + (32 * blk + (lane % 32)) * T::kStride + 32 * c + 16 * hl);
@@ -314,38 +343,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       }
     }
 
-    // ---- dequantize: u = S * ks (plain tiles keep u, the others take t = u*c + lb) ----
+    // ---- dequantize: u = S*ks; plain tiles keep u, the others take t = u*c + lb ----
     float t[2][16];
     float mx;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kk = 32 * blk + 8 * g + 4 * hl;
+        const float4 kv = *(const float4*)(cur.ks + kk);
+        const float4 nv = *(const float4*)(cur.nks + kk);
+        const float kvs[4] = {kv.x, kv.y, kv.z, kv.w};
+        const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(__int_as_float(s[blk][4 * g + r]), kvs[r], nvs[r]);
+      }
     if (plain) {
-      float um = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 kv = *(const float4*)(cur.ks + 32 * blk + 8 * g + 4 * hl);
-          t[blk][4 * g + 0] = (float)s[blk][4 * g + 0] * kv.x;
-          t[blk][4 * g + 1] = (float)s[blk][4 * g + 1] * kv.y;
-          t[blk][4 * g + 2] = (float)s[blk][4 * g + 2] * kv.z;
-          t[blk][4 * g + 3] = (float)s[blk][4 * g + 3] * kv.w;
-          um = max3(max3(um, t[blk][4 * g], t[blk][4 * g + 1]), t[blk][4 * g + 2], t[blk][4 * g + 3]);
-        }
-      mx = xmax32(um) * crow;     // crow >= 0, so max(u)*c = max(u*c)
+      mx = xmax32(max32(t)) * crow;     // crow >= 0, so max(u)*c = max(u*c)
     } else {
-      float tm = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 kv = *(const float4*)(cur.ks + 32 * blk + 8 * g + 4 * hl);
           const float4 bv = *(const float4*)(cur.lb + 32 * blk + 8 * g + 4 * hl);
-          t[blk][4 * g + 0] = fmaf((float)s[blk][4 * g + 0] * kv.x, crow, bv.x);
-          t[blk][4 * g + 1] = fmaf((float)s[blk][4 * g + 1] * kv.y, crow, bv.y);
-          t[blk][4 * g + 2] = fmaf((float)s[blk][4 * g + 2] * kv.z, crow, bv.z);
-          t[blk][4 * g + 3] = fmaf((float)s[blk][4 * g + 3] * kv.w, crow, bv.w);
-          tm = max3(max3(tm, t[blk][4 * g], t[blk][4 * g + 1]), t[blk][4 * g + 2], t[blk][4 * g + 3]);
+          const float bvs[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(t[blk][4 * g + r], crow, bvs[r]);
         }
-      mx = xmax32(tm);
+      mx = xmax32(max32(t));
     }
 
     // ---- lazy rescale: only when a row max passes the reference by the slack ----
@@ -362,7 +387,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     // plain tiles hold u and need t = u*c; the others already hold t
     const float tscale = plain ? crow : 1.0f;
 
-    // ---- p = exp2(t - m) as packed P^T operands, row sum on the packed values, PV ----
+    // ---- p = exp2(t - m) as packed P^T operands, fp32 row sum, PV ----
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
@@ -403,7 +428,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       }
     }
 
-    if (iter + 1 < it.n) lstore(sm[(iter + 1) & 1]);
+    if (more) lstore(nxt);
     __syncthreads();
   }
 
