@@ -83,48 +83,38 @@ __device__ __forceinline__ float load_bias(const void* p, int dtype, int64_t idx
   return dtype == BF16 ? bf16_bits_to_float(h) : half_bits_to_float(h);
 }
 
-// Key-tile iteration: either the tiles covering up to 4 key segments, or the
-// key-tile list of this query tile (block-sparse). Every field is uniform
-// across the block; plain scalars (no arrays) keep them in SGPRs.
-struct TileIter {
-  int n;                                  // number of tiles
-  int t0_0, t0_1, t0_2, t0_3;             // first tile of each segment
-  int n_0, n_1, n_2;                      // tiles of segments 0..2 (segment 3 takes the rest)
-  int lo_0, lo_1, lo_2, lo_3, hi_0, hi_1, hi_2, hi_3;
-  const int32_t* list;                    // sparse: key tiles
-  const int32_t* vbs;                     // sparse: valid counts (nullable)
-  int ntiles_k;                           // sparse: number of key tiles
-
-  // tile index and the valid key range [lo, hi) inside it (absolute keys).
-  // A listed tile outside [0, ntiles_k) is treated as an empty tile.
-  __device__ __forceinline__ void get(int it, int& tile, int& lo, int& hi) const {
-    if (list) {
-      tile = __builtin_amdgcn_readfirstlane(list[it]);
-      if (tile < 0 || tile >= ntiles_k) {
-        tile = 0;
-        lo = hi = 0;
-        return;
-      }
-      lo = tile * BN;
-      hi = lo + (vbs ? min(max(__builtin_amdgcn_readfirstlane(vbs[tile]), 0), BN) : BN);
+// Key tile `it` of a call and the key range [lo, hi) attended inside it
+// (absolute keys, inside [0, Sk)). Dense calls walk the tiles covering up to
+// 4 key segments in order; block-sparse calls walk the query tile's list,
+// where a listed tile outside [0, ntk) counts as an empty tile. Everything
+// here is wave-uniform and lives in SGPRs.
+template <bool SPARSE>
+__device__ __forceinline__ void tile_at(const AttnArgs& a, const int32_t* list, int ntk, int it, int& tile,
+                                        int& lo, int& hi) {
+  if constexpr (SPARSE) {
+    tile = __builtin_amdgcn_readfirstlane(list[it]);
+    if (tile < 0 || tile >= ntk) {
+      tile = 0;
+      lo = hi = 0;
       return;
     }
-    int t0, slo, shi;
-    if (it < n_0) {
-      t0 = t0_0; slo = lo_0; shi = hi_0;
-    } else if ((it -= n_0) < n_1) {
-      t0 = t0_1; slo = lo_1; shi = hi_1;
-    } else if ((it -= n_1) < n_2) {
-      t0 = t0_2; slo = lo_2; shi = hi_2;
-    } else {
-      it -= n_2;
-      t0 = t0_3; slo = lo_3; shi = hi_3;
+    lo = tile * BN;
+    hi = lo + (a.vbs ? min(max(__builtin_amdgcn_readfirstlane(a.vbs[tile]), 0), BN) : BN);
+  } else {
+    int t0 = a.seg_t0[0], slo = a.seg_lo[0], shi = a.seg_hi[0], base = 0;
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      const bool past = it >= a.seg_cum[g];
+      t0 = past ? a.seg_t0[g] : t0;
+      slo = past ? a.seg_lo[g] : slo;
+      shi = past ? a.seg_hi[g] : shi;
+      base = past ? a.seg_cum[g] : base;
     }
-    tile = t0 + it;
+    tile = t0 + it - base;
     lo = max(slo, tile * BN);
     hi = min(shi, tile * BN + BN);
   }
-};
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
@@ -165,65 +155,163 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// ---- LDS tiles ------------------------------------------------------------
+// Tiles are copied from global memory straight into LDS (buffer loads with
+// the LDS destination: each load instruction writes 64 lanes x 16 bytes,
+// lane after lane, from a wave-uniform LDS base). Rows are therefore stored
+// unpadded, and bank conflicts of the operand reads are avoided by XOR-ing
+// the 16-byte chunk index with a function of the row:
+//  K8 rows (D bytes, D/16 chunks): the MFMA A-operand read hands 16 lanes 16
+//    rows of one chunk; chunk ^= (row / (256/D)) mod (D/16) puts them on 16
+//    different 16-byte bank groups.
+//  V rows (2D bytes, D/8 chunks): ds_read_b64_tr_b16 hands a 16-lane group
+//    4 consecutive rows of one 32-byte window; chunk ^= (row mod 4) *
+//    (D/32) moves the 4 windows apart.
 template <int D>
-struct Smem {
-  unsigned char k[BN * Tile<D>::kStride];
-  unsigned char v[BN * Tile<D>::vStride];
-  float ks[BN];   // key scales
-  float nks[BN];  // -kMagic * ks: turns the biased accumulator into S*ks with one FMA
-  float lb[BN];   // log2-domain additive term per key: bias*log2(e), or -inf for an excluded key
+__device__ __forceinline__ int k_chunk_pos(int row, int chunk) {
+  constexpr int kChunks = D / 16, kRowsPer256 = 256 / D;
+  return chunk ^ ((row / kRowsPer256) & (kChunks - 1));
+}
+template <int D>
+__device__ __forceinline__ int v_chunk_pos(int row, int chunk) {
+  return chunk ^ ((row & 3) * (D / 32));
+}
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (raw addressing, range-checked:
+// a lane whose offset is at or past the size reads zero).
+__device__ __forceinline__ v4u buf_desc(const void* base, int64_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const unsigned n = bytes <= 0 ? 0u : (bytes >= 0x7fffffff ? 0x7fffffffu : (unsigned)bytes);
+  return v4u{(unsigned)p, (unsigned)(p >> 32) & 0xffffu, n, 0x00020000u};
+}
+
+// LDS byte address of a shared-memory location.
+template <typename T>
+__device__ __forceinline__ unsigned lds_addr(const T* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
+}
+
+// Global -> LDS copy of one lane-linear block: lane l's SIZE bytes (16, 4,
+// or 2 zero-extended to 4) land at lds + l*max(SIZE,4). Written as inline
+// assembly so that the compiler neither waits on these copies before
+// unrelated LDS reads nor counts them: every wait for them is explicit
+// (wait_vmcnt / stage_barrier), and the loop issues no other vector-memory
+// instruction, so those waits count exactly these copies.
+template <int SIZE>
+__device__ __forceinline__ void lds_copy(unsigned lds, int voff, v4u desc) {
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
+  else if constexpr (SIZE == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
+}
+
+// Per-key terms of one tile: sc[0] key scale ks, sc[1] = -kMagic*ks (turns
+// the biased accumulator into S*ks with one FMA), sc[2] log2-domain additive
+// term (bias*log2(e) for a biased call, 0 otherwise; -inf for an excluded
+// key), sc[3] unused. Wave 0 copies the key scales into raw[0] and derives
+// sc[0], sc[1]; wave 1 copies the bias values into raw[1] and derives sc[2].
+struct KeyTerms {
+  float sc[4][BN];
+  uint32_t raw[2][BN];
 };
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmem = 0x020, kSgDsRead = 0x100;
+
+// At most N vector-memory operations (copies) of this wave outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// All LDS operations of this wave done, at most N vector-memory operations
+// (and LDS copies) of this wave outstanding, then the workgroup barrier. The
+// asm memory clobber keeps the compiler from moving memory accesses across
+// it; the (at most N) LDS copies still in flight target stages nobody reads before the
+// next barrier.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
 
 // LSE is a compile-time trait: the LSE store exists only in the instances
 // that return it, so the plain kernels carry no runtime branch for it.
+//
+// Software pipeline, per 64-key tile j (one barrier per tile). LDS holds
+// three stages of K8, V and key terms; at the start of iteration j, K(j+1),
+// V(j) and the terms of tiles j, j+1 are in LDS, S(j) is in registers, and
+// the copies of K(j+2) and V(j+1) are in flight.
+//   A  dequantize S(j) while the int8 MFMAs of S(j+1) = K8(j+1) Q8^T run;
+//      start the copies of K(j+3) and V(j+2); row max; lazy rescale.
+//   B  p = exp2(t - m) one 16-key chunk at a time, packed to V's type, row
+//      sum, and the bf16 MFMAs O^T += V^T P^T of that chunk.
+//   C  write the key terms of tile j+2 (fetched during the tile); wait for
+//      this wave's copies of K(j+2) and V(j+1); barrier.
+// Copies past the end of the tile list use empty buffer ranges and write
+// zeros, and the MFMAs of a tile past the end run on those zeros, so the
+// loop body has no branch besides the rescale.
 template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int KC = D / 32;                       // int8 MFMA k-steps / 32-channel blocks
-  constexpr int K_CHUNKS = BN * D / 16;            // 16-byte chunks in a K8 tile
-  constexpr int V_CHUNKS = BN * D * 2 / 16;        // 16-byte chunks in a V tile
-  constexpr int K_PER_T = K_CHUNKS / NT;
-  constexpr int V_PER_T = V_CHUNKS / NT;
-  static_assert(K_CHUNKS % NT == 0 && V_CHUNKS % NT == 0, "tile split");
-  using T = Tile<D>;
+  constexpr int KC = D / 32;                     // int8 MFMA k-steps / 32-channel blocks
+  constexpr int NSTG = 3;                        // LDS stages
+  constexpr int K_BYTES = BN * D, V_BYTES = BN * 2 * D;
+  constexpr int KI = K_BYTES / 1024, VI = V_BYTES / 1024;   // 1 KB copy instructions per tile
+  constexpr int KI_W = KI / NW, VI_W = VI / NW;            // ... per wave
+  constexpr int K_ROWS_I = 1024 / D, V_ROWS_I = 1024 / (2 * D);   // rows per copy instruction
+  constexpr int N_COPY_W = KI_W + VI_W;                    // copy instructions per wave per tile
+  static_assert(KI % NW == 0 && VI % NW == 0, "copy split");
   typedef typename std::conditional<VT == BF16, v8bf, v8h>::type pvec;
 
-  // two stages: tile i is computed from one while tile i+1 is written to the other
-  __shared__ __attribute__((aligned(16))) Smem<D> sm[2];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[NSTG][K_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NSTG][V_BYTES];
+  __shared__ __attribute__((aligned(16))) KeyTerms kt[NSTG];
 
   const int bid = xcd_remap((int)blockIdx.x, total_blocks);
   const int bh = bid / qtiles, qt = bid % qtiles;
   const int b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hl = lane / 32;          // k-group of this lane in the MFMA operands
   const int q = qt * BM + wave * 32 + (lane % 32);
   const bool qvalid = q < a.Sq;
   const int64_t qrow = (int64_t)bh * a.Sq + q;
 
-  // ---- tile list ----
-  TileIter it{};
-  if (SPARSE) {
-    const int T = a.Sk / BN;
-    it.list = a.index + ((int64_t)bh * T + qt) * T;
-    it.vbs = a.vbs;
-    it.ntiles_k = T;
-    it.n = min(max(__builtin_amdgcn_readfirstlane(a.count[(int64_t)bh * T + qt]), 0), T);
+  // ---- tile list (scalar loads: the lists are read-only here) ----
+  const __attribute__((address_space(4))) int32_t* list = nullptr;
+  int ntk = 0, n_tiles;
+  if constexpr (SPARSE) {
+    ntk = a.Sk / BN;
+    list = (const __attribute__((address_space(4))) int32_t*)(a.index + ((int64_t)bh * ntk + qt) * ntk);
+    const int cnt = ((const __attribute__((address_space(4))) int32_t*)a.count)[(int64_t)bh * ntk + qt];
+    n_tiles = min(max(cnt, 0), ntk);
   } else {
-    // segments beyond nseg are empty; the host passes at least one
-    auto seg = [&](int g, int& t0, int& n, int& lo, int& hi) {
-      lo = g < a.nseg ? a.seg_lo[g] : 0;
-      hi = g < a.nseg ? a.seg_hi[g] : 0;
-      t0 = lo / BN;
-      n = hi > lo ? (hi + BN - 1) / BN - t0 : 0;
-    };
-    int n3;
-    seg(0, it.t0_0, it.n_0, it.lo_0, it.hi_0);
-    seg(1, it.t0_1, it.n_1, it.lo_1, it.hi_1);
-    seg(2, it.t0_2, it.n_2, it.lo_2, it.hi_2);
-    seg(3, it.t0_3, n3, it.lo_3, it.hi_3);
-    it.n = it.n_0 + it.n_1 + it.n_2 + n3;
+    n_tiles = a.seg_ntiles;
   }
+  const __attribute__((address_space(4))) int32_t* vbs = (const __attribute__((address_space(4))) int32_t*)a.vbs;
+  // key tile i of this block and the key range [lo, hi) attended inside it
+  auto get = [&](int i, int& tile, int& lo, int& hi) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      tile = list[i];
+      if (tile < 0 || tile >= ntk) {
+        tile = 0;
+        lo = hi = 0;
+        return;
+      }
+      lo = tile * BN;
+      hi = lo + (vbs ? min(max(vbs[tile], 0), BN) : BN);
+    } else {
+      tile_at<false>(a, nullptr, 0, i, tile, lo, hi);
+    }
+  };
 
   // ---- Q codes for this lane's row: kept in VGPRs for the whole key loop ----
   v4i qreg[KC];
@@ -232,63 +320,82 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     if (qvalid) qreg[c] = *(const v4i*)(a.q8 + qrow * D + 32 * c + 16 * hl);
     else qreg[c] = v4i{0, 0, 0, 0};
   }
-  const float crow = qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f;
+  // row factor of the log2-domain logits; kept above zero so that an
+  // excluded key (-inf) stays -inf when scaled (a zero row's logits are 0
+  // either way)
+  const float crow = fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f);
 
-  // ---- per-(b,h) sources; every tile load is a range-checked buffer load ----
+  // ---- per-(b,h) sources; every copy and load is range-checked ----
   const unsigned char* kbase = (const unsigned char*)(a.k8 + (int64_t)bh * a.Sk * D);
-  const int64_t k_bytes = (int64_t)a.Sk * D;
+  const int64_t k_total = (int64_t)a.Sk * D;
   const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * 2;
-  const int64_t v_bytes = a.Sk > 0 ? ((int64_t)(a.Sk - 1) * a.v_ss + D) * 2 : 0;
+  const int64_t v_total = a.Sk > 0 ? ((int64_t)(a.Sk - 1) * a.v_ss + D) * 2 : 0;
   const int v_row = (int)(a.v_ss * 2);
   const float* ksbase = a.ks + (int64_t)bh * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
+  const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
 
-  // per-thread constant offsets inside a tile
-  int k_off[K_PER_T], v_off[V_PER_T], k_lds[K_PER_T], v_lds[V_PER_T];
+  // per-lane source offsets of this wave's copy instructions (tile-relative)
+  int k_src[KI_W], v_src[VI_W];
 #pragma unroll
-  for (int i = 0; i < K_PER_T; ++i) {
-    const int c = tid + i * NT, row = c / (D / 16), col = c % (D / 16);
-    k_off[i] = row * D + col * 16;
-    k_lds[i] = row * T::kStride + col * 16;
+  for (int i = 0; i < KI_W; ++i) {
+    const int ins = wave + i * NW;
+    const int row = ins * K_ROWS_I + lane / (D / 16), pos = lane % (D / 16);
+    // LDS chunk `pos` of this row holds source chunk c with k_chunk_pos(row, c) == pos
+    k_src[i] = row * D + k_chunk_pos<D>(row, pos) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < V_PER_T; ++i) {
-    const int c = tid + i * NT, row = c / (D / 8), col = c % (D / 8);
-    v_off[i] = row * v_row + col * 16;
-    v_lds[i] = row * T::vStride + col * 16;
+  for (int i = 0; i < VI_W; ++i) {
+    const int ins = wave + i * NW;
+    const int row = ins * V_ROWS_I + lane / (D / 8), pos = lane % (D / 8);
+    v_src[i] = row * v_row + v_chunk_pos<D>(row, pos) * 16;
   }
 
-  // ---- staging registers for one tile ----
-  uint4 kreg[K_PER_T], vreg[V_PER_T];
-  float ksreg = 0.0f, lbreg = 0.0f;
-
-  auto gload = [&](int tile, int lo, int hi) {
-    const int key0 = __builtin_amdgcn_readfirstlane(tile * BN);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * D, k_bytes - (int64_t)key0 * D);
-    const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc(vbase + (int64_t)key0 * v_row, v_bytes - (int64_t)key0 * v_row);
+  // K8 / V rows of a tile into a stage (zeros when `valid` is false)
+  auto copy_k = [&](int stage, int tile, bool valid) __attribute__((always_inline)) {
+    const int key0 = tile * BN;
+    const v4u d = buf_desc(kbase + (int64_t)key0 * D, valid ? k_total - (int64_t)key0 * D : 0);
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) kreg[i] = bload16(kr, k_off[i]);
+    for (int i = 0; i < KI_W; ++i) lds_copy<16>(lds_addr(&kbuf[stage][(wave + i * NW) * 1024]), k_src[i], d);
+  };
+  auto copy_v = [&](int stage, int tile, bool valid) __attribute__((always_inline)) {
+    const int key0 = tile * BN;
+    const v4u d = buf_desc(vbase + (int64_t)key0 * v_row, valid ? v_total - (int64_t)key0 * v_row : 0);
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) vreg[i] = bload16(vr, v_off[i]);
-    if (tid < BN) {
-      const int key = key0 + tid;
-      const bool in = key >= lo && key < hi;   // [lo, hi) lies inside [0, Sk)
-      ksreg = in ? ksbase[key] : 0.0f;
-      float lbv = 0.0f;
-      if (HAS_BIAS && in) lbv = load_bias(a.bias, a.bias_dtype, bias_off + key) * kLog2e;
-      lbreg = in ? lbv : -INFINITY;
+    for (int i = 0; i < VI_W; ++i) lds_copy<16>(lds_addr(&vbuf[stage][(wave + i * NW) * 1024]), v_src[i], d);
+  };
+  // raw key terms of a tile: wave 0 copies the key scales of keys
+  // key0 + lane, wave 1 the bias values (range [lo, hi): keys outside it
+  // read zero and are excluded when the terms are derived)
+  auto copy_terms = [&](int stage, int tile, int lo, int hi, bool valid) __attribute__((always_inline)) {
+    const int nk = valid ? hi - lo : 0;
+    const int rel = tile * BN + lane - lo;   // negative offsets wrap and read as out of range
+    if (wave == 0) {
+      lds_copy<4>(lds_addr(&kt[stage].raw[0][0]), rel * 4, buf_desc(ksbase + lo, (int64_t)nk * 4));
+    } else if (HAS_BIAS && wave == 1) {
+      const v4u d = buf_desc((const unsigned char*)a.bias + (bias_off + lo) * bias_esz, (int64_t)nk * bias_esz);
+      if (bias_esz == 4) lds_copy<4>(lds_addr(&kt[stage].raw[1][0]), rel * 4, d);
+      else lds_copy<2>(lds_addr(&kt[stage].raw[1][0]), rel * 2, d);
     }
   };
-  auto lstore = [&](Smem<D>& s) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) *(uint4*)(s.k + k_lds[i]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) *(uint4*)(s.v + v_lds[i]) = vreg[i];
-    if (tid < BN) {
-      s.ks[tid] = ksreg;
-      s.nks[tid] = -kMagic * ksreg;
-      s.lb[tid] = lbreg;
+  // derive the terms of a tile from its copied raw values (the calling
+  // wave's own copy must have landed)
+  auto derive_terms = [&](int stage, int tile, int lo, int hi) __attribute__((always_inline)) {
+    const int key = tile * BN + lane;
+    const bool in = key >= lo && key < hi;
+    if (wave == 0) {
+      const float ks = in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f;
+      kt[stage].sc[0][lane] = ks;
+      kt[stage].sc[1][lane] = -kMagic * ks;
+    } else if (wave == 1) {
+      float lb = 0.0f;
+      if (HAS_BIAS) {
+        const uint32_t r = kt[stage].raw[1][lane];
+        lb = a.bias_dtype == FP32 ? __uint_as_float(r)
+                                  : (a.bias_dtype == BF16 ? bf16_bits_to_float(r) : half_bits_to_float(r));
+        lb *= kLog2e;
+      }
+      kt[stage].sc[2][lane] = in ? lb : -INFINITY;
     }
   };
 
@@ -299,79 +406,99 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   float m_run = -INFINITY;
   float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ds_read_b64_tr_b16 source addressing (per 16-lane group): lane s of the
-  // group reads 4 channels at (key0 + s/4, dbase + 4*(s%4)); the hardware
-  // hands lane i of the group the 4 keys of channel dbase + i.
+  // operand addressing
   const int grp = lane / 16, sl = lane % 16;
-  const int tr_row = 4 * hl + sl / 4;
-  const int tr_col = 16 * (grp % 2) + 4 * (sl % 4);
+  const int tr_row = 4 * hl + sl / 4;                     // ds_read_b64_tr_b16 source row (+ tile row base)
+  const int tr_byte = 2 * (16 * (grp % 2) + 4 * (sl % 4));  // ... and byte inside a 64-byte channel block
 
-  if (it.n > 0) {
-    int tile, lo, hi;
-    it.get(0, tile, lo, hi);
-    gload(tile, lo, hi);
-    lstore(sm[0]);
-    __syncthreads();
+  // S^T = K8 Q8^T of one 32-key block; accumulators start at kMagicBits
+  v16i s[2];
+  auto qk_block = [&](int stage, int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[blk][r] = kMagicBits;
+    const int row = 32 * blk + lane % 32;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const v4i kv = *(const v4i*)(&kbuf[stage][row * D + k_chunk_pos<D>(row, 2 * c + hl) * 16]);
+      s[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qreg[c], s[blk], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue: K(0), K(1), V(0) and the terms of tiles 0, 1 in LDS; S(0) ----
+  {
+    int t0 = 0, l0 = 0, h0 = 0, t1 = 0, l1 = 0, h1 = 0;
+    if (n_tiles > 0) get(0, t0, l0, h0);
+    if (n_tiles > 1) get(1, t1, l1, h1);
+    copy_terms(0, t0, l0, h0, n_tiles > 0);
+    copy_terms(1, t1, l1, h1, n_tiles > 1);
+    copy_k(0, t0, n_tiles > 0);
+    copy_v(0, t0, n_tiles > 0);
+    copy_k(1, t1, n_tiles > 1);
+    wait_vmcnt<0>();
+    derive_terms(0, t0, l0, h0);
+    derive_terms(1, t1, l1, h1);
+    stage_barrier<0>();
+    qk_block(0, 0);
+    qk_block(0, 1);
+    // every wave's reads of K(0) are done before stage 0 is refilled
+    stage_barrier<0>();
+    int t2 = 0, l2 = 0, h2 = 0;
+    if (n_tiles > 2) get(2, t2, l2, h2);
+    copy_k(2, t2, n_tiles > 2);
+    copy_v(1, t1, n_tiles > 1);
   }
 
-  // one key tile per iteration: tile `iter` is in `cur`; tile iter+1 is
-  // fetched meanwhile and written to `nxt`
-  for (int iter = 0; iter < it.n; ++iter) {
-    Smem<D>& cur = sm[iter & 1];
-    Smem<D>& nxt = sm[(iter + 1) & 1];
-    int tile, lo, hi;
-    it.get(iter, tile, lo, hi);
-    // unmasked tile without bias: scores need no additive term
-    const bool plain = !HAS_BIAS && lo == tile * BN && hi == tile * BN + BN;
-    const bool more = iter + 1 < it.n;
-    if (more) {
-      int t2, l2, h2;
-      it.get(iter + 1, t2, l2, h2);
-      gload(t2, l2, h2);
-    }
+  // One tile. `edge` tiles of an unbiased call hold excluded keys (segment
+  // edges, block-sparse tiles); they take the additive term (0 or -inf) in
+  // a short uniform branch, so every tile runs the same code otherwise.
+  auto tile_body = [&](int iter, int st0, int st1, int st2, bool edge) __attribute__((always_inline)) {
+    // st0 = iter % 3, st1 = (iter + 1) % 3, st2 = (iter + 2) % 3
+    const KeyTerms& tc = kt[st0];
+    int t3 = 0, l3 = 0, h3 = 0, t2 = 0, l2 = 0, h2 = 0;
+    if (iter + 3 < n_tiles) get(iter + 3, t3, l3, h3);
+    if (iter + 2 < n_tiles) get(iter + 2, t2, l2, h2);
+    copy_terms(st2, t2, l2, h2, iter + 2 < n_tiles);
 
-    // ---- S^T = K8 Q8^T: two 32-key blocks, accumulators biased by kMagicBits ----
-    v16i s[2];
+    // ===== A: dequantize S(iter); S(iter+1) MFMAs; copies; row max =====
+    // unbiased: t = S*ks (+ lb on edge tiles: 0 or -inf), crow is applied
+    // in the exponent; biased: t = S*ks*crow + lb.
+    float t[2][16];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[blk][r] = kMagicBits;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const v4i kv = *(const v4i*)(cur.k + (32 * blk + (lane % 32)) * T::kStride + 32 * c + 16 * hl);
-        s[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qreg[c], s[blk], 0, 0, 0);
-      }
-    }
-
-    // ---- dequantize: u = S*ks; plain tiles keep u, the others take t = u*c + lb ----
-    float t[2][16];
-    float mx;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int kk = 32 * blk + 8 * g + 4 * hl;
-        const float4 kv = *(const float4*)(cur.ks + kk);
-        const float4 nv = *(const float4*)(cur.nks + kk);
+        const float4 kv = *(const float4*)(&tc.sc[0][kk]);
+        const float4 nv = *(const float4*)(&tc.sc[1][kk]);
         const float kvs[4] = {kv.x, kv.y, kv.z, kv.w};
         const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(__int_as_float(s[blk][4 * g + r]), kvs[r], nvs[r]);
-      }
-    if (plain) {
-      mx = xmax32(max32(t)) * crow;     // crow >= 0, so max(u)*c = max(u*c)
-    } else {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 bv = *(const float4*)(cur.lb + 32 * blk + 8 * g + 4 * hl);
+        if (HAS_BIAS) {
+          const float4 bv = *(const float4*)(&tc.sc[2][kk]);
           const float bvs[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(t[blk][4 * g + r], crow, bvs[r]);
         }
-      mx = xmax32(max32(t));
+      }
+      qk_block(st1, blk);   // the score registers of this block are free again
+      if (blk == 0) copy_k(iter % 3, t3, iter + 3 < n_tiles);   // K(iter+3) over K(iter)
     }
+    copy_v(st2, t2, iter + 2 < n_tiles);                        // V(iter+2) over V(iter-1)
+    if (!HAS_BIAS && edge) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 bv = *(const float4*)(&tc.sc[2][32 * blk + 8 * g + 4 * hl]);
+          t[blk][4 * g + 0] += bv.x;
+          t[blk][4 * g + 1] += bv.y;
+          t[blk][4 * g + 2] += bv.z;
+          t[blk][4 * g + 3] += bv.w;
+        }
+    }
+    // crow > 0, so max(u)*crow = max(u*crow) (also for -inf)
+    const float mx = (HAS_BIAS) ? xmax32(max32(t)) : xmax32(max32(t)) * crow;
 
     // ---- lazy rescale: only when a row max passes the reference by the slack ----
     if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
@@ -384,53 +511,80 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    // plain tiles hold u and need t = u*c; the others already hold t
-    const float tscale = plain ? crow : 1.0f;
 
-    // ---- p = exp2(t - m) as packed P^T operands, fp32 row sum, PV ----
+    // ===== B: p = exp2(t - m) chunk by chunk, row sum, PV MFMAs =====
+    const unsigned char* vcur = vbuf[st0];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int chunk = 0; chunk < 4; ++chunk) {
+      const int blk = chunk / 2, m = chunk % 2;
+      uint32_t pw[4];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        // the row sum takes the fp32 values: a sum of bf16-rounded p would
-        // carry up to 2^-9 relative error into the LSE when one key dominates
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(t[blk][8 * m + 2 * e], tscale, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(t[blk][8 * m + 2 * e + 1], tscale, -m_use));
-          lsum[e] += p0 + p1;
-          if constexpr (VT == BF16) {
-            const v2bf pair = {(__bf16)p0, (__bf16)p1};
-            pw[e] = __builtin_bit_cast(uint32_t, pair);
-          } else {
-            const v2h pair = {(_Float16)p0, (_Float16)p1};
-            pw[e] = __builtin_bit_cast(uint32_t, pair);
-          }
+      for (int e = 0; e < 4; ++e) {
+        float x0, x1;
+        if (HAS_BIAS) {
+          x0 = t[blk][8 * m + 2 * e] - m_use;
+          x1 = t[blk][8 * m + 2 * e + 1] - m_use;
+        } else {
+          x0 = fmaf(t[blk][8 * m + 2 * e], crow, -m_use);
+          x1 = fmaf(t[blk][8 * m + 2 * e + 1], crow, -m_use);
         }
-        const pvec pb = __builtin_bit_cast(pvec, pw);
-        const int krow = 32 * blk + 16 * m + tr_row;
+        const float p0 = __builtin_amdgcn_exp2f(x0);
+        const float p1 = __builtin_amdgcn_exp2f(x1);
+        if constexpr (VT == BF16) {
+          const v2bf pair = {(__bf16)p0, (__bf16)p1};
+          pw[e] = __builtin_bit_cast(uint32_t, pair);
+          // with an LSE the row sum takes the fp32 values (a sum of rounded
+          // p would carry up to 2^-9 relative error into the LSE when one key
+          // dominates); without one it sums the rounded weights PV uses, so
+          // the output is their exact weighted mean
+          if (LSE) lsum[e] += p0 + p1;
+          else lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, v2bf{(__bf16)1.0f, (__bf16)1.0f}, lsum[e], false);
+        } else {
+          const v2h pair = {(_Float16)p0, (_Float16)p1};
+          pw[e] = __builtin_bit_cast(uint32_t, pair);
+          if (LSE) lsum[e] += p0 + p1;
+          else lsum[e] = __builtin_amdgcn_fdot2(pair, v2h{(_Float16)1.0f, (_Float16)1.0f}, lsum[e], false);
+        }
+      }
+      const pvec pb = __builtin_bit_cast(pvec, pw);
+      const int row0 = 32 * blk + 16 * m + tr_row;   // and row0 + 8
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const unsigned char* p0 = cur.v + krow * T::vStride + (32 * c + tr_col) * 2;
-          const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
-          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(p0 + 8 * T::vStride));
-          const v4s both[2] = {lo4, hi4};
-          if constexpr (VT == BF16) {
-            const v8bf av = __builtin_bit_cast(v8bf, both);
-            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[c], 0, 0, 0);
-          } else {
-            const v8h av = __builtin_bit_cast(v8h, both);
-            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, o[c], 0, 0, 0);
-          }
+      for (int c = 0; c < KC; ++c) {
+        const int byte = 64 * c + tr_byte;
+        const int a0 = row0 * (2 * D) + v_chunk_pos<D>(row0, byte / 16) * 16 + byte % 16;
+        const int a1 = (row0 + 8) * (2 * D) + v_chunk_pos<D>(row0 + 8, byte / 16) * 16 + byte % 16;
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vcur + a0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vcur + a1));
+        const v4s both[2] = {lo4, hi4};
+        if constexpr (VT == BF16) {
+          const v8bf av = __builtin_bit_cast(v8bf, both);
+          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[c], 0, 0, 0);
+        } else {
+          const v8h av = __builtin_bit_cast(v8h, both);
+          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, o[c], 0, 0, 0);
         }
       }
     }
 
-    if (more) lstore(nxt);
-    __syncthreads();
+    // ===== C: this wave's copies older than this tile's K/V copies are done;
+    // terms of tile iter+2; barrier =====
+    wait_vmcnt<N_COPY_W>();
+    derive_terms(st2, t2, l2, h2);
+    stage_barrier<N_COPY_W>();
+  };
+
+  int st0 = 0, st1 = 1, st2 = 2;
+  for (int iter = 0; iter < n_tiles; ++iter) {
+    int tile, lo, hi;
+    get(iter, tile, lo, hi);
+    tile_body(iter, st0, st1, st2, lo != tile * BN || hi != tile * BN + BN);
+    const int tmp = st0;
+    st0 = st1;
+    st1 = st2;
+    st2 = tmp;
   }
+  // drain this wave's remaining copies (they target stages nobody reads)
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O_acc / l * v_scale, LSE ----
   const float l_tot = xsum32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
@@ -495,7 +649,16 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  int cum = 0;
+  for (int g = 0; g < 4; ++g) {
+    const bool live = g < a.nseg && a.seg_hi[g] > a.seg_lo[g];
+    a.seg_t0[g] = live ? a.seg_lo[g] / BN : 0;
+    a.seg_cum[g] = g < a.nseg ? cum : INT32_MAX;
+    if (live) cum += (a.seg_hi[g] + BN - 1) / BN - a.seg_lo[g] / BN;
+  }
+  a.seg_ntiles = cum;
   if (a.D == 128) return a.v_dtype == BF16 ? launch_d_vt<128, BF16>(a, s) : launch_d_vt<128, FP16>(a, s);
   return a.v_dtype == BF16 ? launch_d_vt<64, BF16>(a, s) : launch_d_vt<64, FP16>(a, s);
 }

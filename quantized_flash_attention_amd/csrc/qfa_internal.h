@@ -65,6 +65,11 @@ struct AttnArgs {
   const float* v_scale; // nullable [H, D]
   int nseg;
   int seg_lo[4], seg_hi[4];
+  // derived by the launcher from the segments: first key tile of segment g,
+  // number of tiles before segment g (INT32_MAX for absent segments), and
+  // the total number of key tiles of the call
+  int seg_t0[4], seg_cum[4];
+  int seg_ntiles;
   void* out;
   int out_dtype;
   int64_t o_sb, o_sh, o_ss;
