@@ -199,6 +199,11 @@ __device__ __forceinline__ unsigned lds_addr(const T* p) {
 // unrelated LDS reads nor counts them: every wait for them is explicit
 // (wait_vmcnt / stage_barrier), and the loop issues no other vector-memory
 // instruction, so those waits count exactly these copies.
+// M0 is reserved to the compiler, which warns about clobbering it; the
+// kernels of this file make no other use of M0, so nothing is live in it
+// across these statements.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int SIZE>
 __device__ __forceinline__ void lds_copy(unsigned lds, int voff, v4u desc) {
   if constexpr (SIZE == 16)
@@ -211,12 +216,14 @@ __device__ __forceinline__ void lds_copy(unsigned lds, int voff, v4u desc) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
                  :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Per-key terms of one tile: sc[0] key scale ks, sc[1] = -kMagic*ks (turns
-// the biased accumulator into S*ks with one FMA), sc[2] log2-domain additive
-// term (bias*log2(e) for a biased call, 0 otherwise; -inf for an excluded
-// key), sc[3] unused. Wave 0 copies the key scales into raw[0] and derives
-// sc[0], sc[1]; wave 1 copies the bias values into raw[1] and derives sc[2].
+// the biased accumulator into S*ks with one FMA; for an excluded key ks = 0
+// and sc[1] = -inf, so its score comes out -inf), sc[2] log2-domain bias
+// term bias*log2(e) (biased calls only), sc[3] unused. Wave 0 copies the key
+// scales into raw[0] and derives sc[0], sc[1]; wave 1 copies the bias
+// values into raw[1] and derives sc[2].
 struct KeyTerms {
   float sc[4][BN];
   uint32_t raw[2][BN];
@@ -236,10 +243,59 @@ __device__ __forceinline__ void wait_vmcnt() {
 // asm memory clobber keeps the compiler from moving memory accesses across
 // it; the (at most N) LDS copies still in flight target stages nobody reads before the
 // next barrier.
+// sched_barrier(0) on both sides keeps the compiler from moving any
+// instruction (arithmetic included) across the barrier.
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue of one lane's query row: O = O_acc / l * v_scale (RNE to the
+// output type) and, for LSE instances, LSE = (m + log2 l) ln 2 + sm_scale*qmu
+// (-inf for a row with no attended key, whose O is 0).
+template <int D, bool LSE>
+__device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D / 32], const float (&lsum)[4],
+                                           float m_run, int b, int h, int q, int64_t qrow, bool qvalid, int hl) {
+  const float l_tot = xsum32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+  if (!qvalid) return;
+  const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)q * a.o_ss;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * c + 8 * g + 4 * hl;
+      float vals[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vals[r] = o[c][4 * g + r] * inv_l;
+      if (a.v_scale) {
+        const float4 vs = *(const float4*)(a.v_scale + (int64_t)h * D + d0);
+        vals[0] *= vs.x; vals[1] *= vs.y; vals[2] *= vs.z; vals[3] *= vs.w;
+      }
+      if (a.out_dtype == FP32) {
+        *(float4*)((float*)a.out + obase + d0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+      } else if (a.out_dtype == BF16) {
+        const uint32_t w0 = float_to_bf16_bits(vals[0]) | (float_to_bf16_bits(vals[1]) << 16);
+        const uint32_t w1 = float_to_bf16_bits(vals[2]) | (float_to_bf16_bits(vals[3]) << 16);
+        *(uint2*)((uint16_t*)a.out + obase + d0) = make_uint2(w0, w1);
+      } else {
+        const uint32_t w0 = float_to_half_bits(vals[0]) | (float_to_half_bits(vals[1]) << 16);
+        const uint32_t w1 = float_to_half_bits(vals[2]) | (float_to_half_bits(vals[3]) << 16);
+        *(uint2*)((uint16_t*)a.out + obase + d0) = make_uint2(w0, w1);
+      }
+    }
+  }
+  if (LSE && hl == 0) {
+    float L = -INFINITY;
+    if (l_tot > 0.0f) {
+      L = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      if (a.qmu) L += a.sm_scale * a.qmu[qrow];
+    }
+    a.lse[qrow] = L;
+  }
 }
 
 // LSE is a compile-time trait: the LSE store exists only in the instances
@@ -386,16 +442,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     if (wave == 0) {
       const float ks = in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f;
       kt[stage].sc[0][lane] = ks;
-      kt[stage].sc[1][lane] = -kMagic * ks;
-    } else if (wave == 1) {
-      float lb = 0.0f;
-      if (HAS_BIAS) {
-        const uint32_t r = kt[stage].raw[1][lane];
-        lb = a.bias_dtype == FP32 ? __uint_as_float(r)
-                                  : (a.bias_dtype == BF16 ? bf16_bits_to_float(r) : half_bits_to_float(r));
-        lb *= kLog2e;
-      }
-      kt[stage].sc[2][lane] = in ? lb : -INFINITY;
+      // an excluded key dequantizes to fma(x, 0, -inf) = -inf
+      kt[stage].sc[1][lane] = in ? -kMagic * ks : -INFINITY;
+    } else if (HAS_BIAS && wave == 1) {
+      const uint32_t r = kt[stage].raw[1][lane];
+      const float bias = a.bias_dtype == FP32 ? __uint_as_float(r)
+                                              : (a.bias_dtype == BF16 ? bf16_bits_to_float(r) : half_bits_to_float(r));
+      kt[stage].sc[2][lane] = bias * kLog2e;
     }
   };
 
@@ -448,10 +501,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_v(1, t1, n_tiles > 1);
   }
 
-  // One tile. `edge` tiles of an unbiased call hold excluded keys (segment
-  // edges, block-sparse tiles); they take the additive term (0 or -inf) in
-  // a short uniform branch, so every tile runs the same code otherwise.
-  auto tile_body = [&](int iter, int st0, int st1, int st2, bool edge) __attribute__((always_inline)) {
+  // One tile. Excluded keys (segment edges, pad keys of block-sparse tiles)
+  // carry -inf in their key terms, so every tile runs the same code.
+  auto tile_body = [&](int iter, int st0, int st1, int st2) __attribute__((always_inline)) {
     // st0 = iter % 3, st1 = (iter + 1) % 3, st2 = (iter + 2) % 3
     const KeyTerms& tc = kt[st0];
     int t3 = 0, l3 = 0, h3 = 0, t2 = 0, l2 = 0, h2 = 0;
@@ -460,8 +512,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_terms(st2, t2, l2, h2, iter + 2 < n_tiles);
 
     // ===== A: dequantize S(iter); S(iter+1) MFMAs; copies; row max =====
-    // unbiased: t = S*ks (+ lb on edge tiles: 0 or -inf), crow is applied
-    // in the exponent; biased: t = S*ks*crow + lb.
+    // unbiased: t = S*ks, crow is applied in the exponent; biased:
+    // t = S*ks*crow + lb (excluded keys: -inf either way)
     float t[2][16];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -485,18 +537,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       if (blk == 0) copy_k(iter % 3, t3, iter + 3 < n_tiles);   // K(iter+3) over K(iter)
     }
     copy_v(st2, t2, iter + 2 < n_tiles);                        // V(iter+2) over V(iter-1)
-    if (!HAS_BIAS && edge) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 bv = *(const float4*)(&tc.sc[2][32 * blk + 8 * g + 4 * hl]);
-          t[blk][4 * g + 0] += bv.x;
-          t[blk][4 * g + 1] += bv.y;
-          t[blk][4 * g + 2] += bv.z;
-          t[blk][4 * g + 3] += bv.w;
-        }
-    }
     // crow > 0, so max(u)*crow = max(u*crow) (also for -inf)
     const float mx = (HAS_BIAS) ? xmax32(max32(t)) : xmax32(max32(t)) * crow;
 
@@ -575,9 +615,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 
   int st0 = 0, st1 = 1, st2 = 2;
   for (int iter = 0; iter < n_tiles; ++iter) {
-    int tile, lo, hi;
-    get(iter, tile, lo, hi);
-    tile_body(iter, st0, st1, st2, lo != tile * BN || hi != tile * BN + BN);
+    tile_body(iter, st0, st1, st2);
     const int tmp = st0;
     st0 = st1;
     st1 = st2;
@@ -586,45 +624,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // drain this wave's remaining copies (they target stages nobody reads)
   wait_vmcnt<0>();
 
-  // ---- epilogue: O = O_acc / l * v_scale, LSE ----
-  const float l_tot = xsum32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-  if (!qvalid) return;
-  const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)q * a.o_ss;
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * c + 8 * g + 4 * hl;
-      float vals[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vals[r] = o[c][4 * g + r] * inv_l;
-      if (a.v_scale) {
-        const float4 vs = *(const float4*)(a.v_scale + (int64_t)h * D + d0);
-        vals[0] *= vs.x; vals[1] *= vs.y; vals[2] *= vs.z; vals[3] *= vs.w;
-      }
-      if (a.out_dtype == FP32) {
-        *(float4*)((float*)a.out + obase + d0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-      } else if (a.out_dtype == BF16) {
-        const uint32_t w0 = float_to_bf16_bits(vals[0]) | (float_to_bf16_bits(vals[1]) << 16);
-        const uint32_t w1 = float_to_bf16_bits(vals[2]) | (float_to_bf16_bits(vals[3]) << 16);
-        *(uint2*)((uint16_t*)a.out + obase + d0) = make_uint2(w0, w1);
-      } else {
-        const uint32_t w0 = float_to_half_bits(vals[0]) | (float_to_half_bits(vals[1]) << 16);
-        const uint32_t w1 = float_to_half_bits(vals[2]) | (float_to_half_bits(vals[3]) << 16);
-        *(uint2*)((uint16_t*)a.out + obase + d0) = make_uint2(w0, w1);
-      }
-    }
-  }
-  if (LSE && hl == 0) {
-    float L = -INFINITY;
-    if (l_tot > 0.0f) {
-      L = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      if (a.qmu) L += a.sm_scale * a.qmu[qrow];
-    }
-    a.lse[qrow] = L;
-  }
+  store_rows<D, LSE>(a, o, lsum, m_run, b, h, q, qrow, qvalid, hl);
 }
+
 
 template <int D, int VT>
 hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
