@@ -71,7 +71,12 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of head 0 the oracle computes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE passes over "
+                         "this script with --copy-calibration) into " + os.path.relpath(PMC_FILE, ROOT))
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -257,6 +262,71 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, bias32_np, w, core, skirts, args.cpu_rows)
 
     print(json.dumps(out))
+    return 0
+
+
+COPY_BYTES = 256 << 20
+UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false>"
+
+
+def _counter_per_dispatch(path: str, counter: str):
+    """{kernel name: [value per dispatch]} of one rocprofv3 counter_collection.csv (values summed
+    over the rows a dispatch reports, e.g. one per XCD)."""
+    import collections
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    per = collections.defaultdict(float)
+    names = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (f, r["Dispatch_Id"])
+            per[key] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("qfa::", "")
+    out = collections.defaultdict(list)
+    for key, v in per.items():
+        out[names[key]].append(v)
+    return out
+
+
+def pmc_summary(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per unmasked attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain device copy of COPY_BYTES."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(d, needle):
+        vals = [v for n, vs in d.items() if needle in n for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of {needle!r} in the counter files")
+        return statistics.median(vals)
+
+    copy_f, copy_w = pick(fetch, "copyBuffer") * 1024.0, pick(write, "copyBuffer") * 1024.0
+    f_scale, w_scale = COPY_BYTES / copy_f, COPY_BYTES / copy_w
+    un_f, un_w = pick(fetch, UNMASKED_KERNEL) * 1024.0 * f_scale, pick(write, UNMASKED_KERNEL) * 1024.0 * w_scale
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py --cpu-baseline off "
+           "--steps 2 --warmup 1 --variant-iters 1 --copy-calibration")
+    out = {
+        "what": "HBM bytes per launch of the unmasked banded attention call (B1 H56 Sq4096 Sk33600 D128 bf16)",
+        "kernel": UNMASKED_KERNEL,
+        "source_sha256_16": src_hash(ATTN_SRC),
+        "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
+                     "python3 bench.py --pmc-summary <fetch dir> <write dir>"],
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter_bytes": copy_f, "write_counter_bytes": copy_w,
+                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "launches": {"unmasked": {"fetch_bytes": round(un_f), "write_bytes": round(un_w),
+                                  "hbm_bytes_per_launch": round(un_f + un_w)}},
+    }
+    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
+    with open(PMC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out["launches"]["unmasked"]))
     return 0
 
 
