@@ -174,6 +174,22 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  float* lse, void* stream);
 
 /*
+ * qfa_qk_scores_i32 — the int32 scores S = Q8 K8^T exactly as the attention
+ * kernel computes them (FastVideo "minimax_h3_sparse_int8": int8 QK with
+ * integer accumulation), for checking them bit for bit. The call runs the
+ * attention kernel's own tile copies, LDS layout and int8 MFMA path and
+ * stores every score instead of taking the softmax.
+ *
+ * q8:  int8 [B,H,Sq,D] contiguous (from qfa_quantize_qk).
+ * k8:  int8 [B,H,Sk,D] contiguous.
+ * s32: int32 [B,H,Sq,Sk] contiguous output, S[b,h,i,j] = sum_c q8[b,h,i,c]*k8[b,h,j,c]
+ *      (exact: |S| <= 128*127^2 < 2^31).
+ * All three 16-byte aligned; D must be 64 or 128.
+ */
+int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                      const int8_t* q8, const int8_t* k8, int32_t* s32, void* stream);
+
+/*
  * qfa_lse_merge — exact merge of two partial softmaxes over disjoint key sets
  * (comfy-kitchen issue #177, Question 2; FlyDSL PR #886, split-K combine):
  *   m = max(La, Lb); m = -inf -> O = 0, L = -inf;

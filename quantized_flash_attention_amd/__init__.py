@@ -10,6 +10,7 @@ Functions (same names as the C entry points without the ``qfa_`` prefix):
   blockmask_to_index(mask)                         -> (index, count)
   attn_fwd(qk, v, ...)                             -> out or (out, lse)
   lse_merge(o_a, lse_a, o_b, lse_b)                -> (out, lse)
+  qk_scores_i32(q8, k8)                            -> int32 scores of the attention kernel's QK stage
 plus ``int8_attention``, the quantize + attend convenience call.
 """
 from __future__ import annotations
@@ -23,7 +24,7 @@ from . import _lib
 from ._lib import QFA_BF16, QFA_FP16, QFA_FP32, QFAError
 
 __all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
-           "quantize_workspace_bytes"]
+           "quantize_workspace_bytes", "qk_scores_i32"]
 
 _DT = {torch.bfloat16: QFA_BF16, torch.float16: QFA_FP16, torch.float32: QFA_FP32}
 
@@ -111,6 +112,21 @@ def blockmask_to_index(mask: torch.Tensor):
     _lib.check(_lib.lib().qfa_blockmask_to_index(_ptr(m), B, H, Tq, Tk, _ptr(index), _ptr(count),
                                                  _stream(m.device)))
     return index, count
+
+
+def qk_scores_i32(q8: torch.Tensor, k8: torch.Tensor) -> torch.Tensor:
+    """int32 [B,H,Sq,Sk] scores Q8 K8^T computed by the attention kernel's own QK stage."""
+    _no_grad(q8, k8)
+    if q8.dim() != 4 or k8.dim() != 4 or q8.dtype != torch.int8 or k8.dtype != torch.int8:
+        raise ValueError("q8, k8 must be int8 [B,H,S,D]")
+    B, H, Sq, D = q8.shape
+    if k8.shape[0] != B or k8.shape[1] != H or k8.shape[3] != D:
+        raise ValueError(f"k8 shape {tuple(k8.shape)} does not match q8 {tuple(q8.shape)}")
+    Sk = k8.shape[2]
+    q8c, k8c = q8.contiguous(), k8.contiguous()
+    s32 = torch.empty((B, H, Sq, Sk), dtype=torch.int32, device=q8.device)
+    _lib.check(_lib.lib().qfa_qk_scores_i32(B, H, Sq, Sk, D, _ptr(q8c), _ptr(k8c), _ptr(s32), _stream(q8.device)))
+    return s32
 
 
 def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,

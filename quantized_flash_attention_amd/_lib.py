@@ -24,6 +24,7 @@ EXPORTS = (
     "qfa_blockmask_to_index",
     "qfa_attn_fwd",
     "qfa_lse_merge",
+    "qfa_qk_scores_i32",
 )
 
 _P = ctypes.c_void_p
@@ -58,6 +59,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_lse_merge.argtypes = ([_I64] * 4 + [_P, _I, _I64, _I64, _I64, _P] * 2
                                 + [_P, _I, _I64, _I64, _I64, _P, _P])
     L.qfa_lse_merge.restype = _I
+    L.qfa_qk_scores_i32.argtypes = [_I64] * 5 + [_P, _P, _P, _P]
+    L.qfa_qk_scores_i32.restype = _I
 
 
 def lib() -> ctypes.CDLL:

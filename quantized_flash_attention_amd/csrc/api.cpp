@@ -221,6 +221,25 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
   return hip_status(qfa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
 }
 
+int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                      const int8_t* q8, const int8_t* k8, int32_t* s32, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if (B * H * Sq == 0 || Sk == 0) return ok();  // no scores
+  if (!q8 || !k8 || !s32) return fail(QFA_ERR_INVALID_ARG, "q8/k8/s32 is NULL");
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(s32))
+    return fail(QFA_ERR_INVALID_ARG, "q8, k8 and s32 must be 16-byte aligned");
+  if (B * H * Sq * Sk > (1ll << 40)) return fail(QFA_ERR_UNSUPPORTED, "score tensor too large");
+  qfa::AttnArgs a{};
+  a.B = (int)B; a.H = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
+  a.q8 = q8; a.k8 = k8;
+  a.nseg = 1;
+  a.seg_lo[0] = 0;
+  a.seg_hi[0] = (int)Sk;
+  a.out = s32;
+  return hip_status(qfa::launch_qk_scores(a, (hipStream_t)stream), "qk_scores launch");
+}
+
 int qfa_lse_merge(int64_t B, int64_t H, int64_t S, int64_t D,
                   const void* o_a, int a_dtype, int64_t a_sb, int64_t a_sh, int64_t a_ss, const float* lse_a,
                   const void* o_b, int b_dtype, int64_t b_sb, int64_t b_sh, int64_t b_ss, const float* lse_b,

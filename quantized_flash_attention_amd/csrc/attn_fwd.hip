@@ -314,7 +314,13 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 // Copies past the end of the tile list use empty buffer ranges and write
 // zeros, and the MFMAs of a tile past the end run on those zeros, so the
 // loop body has no branch besides the rescale.
-template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE>
+//
+// DUMP instances (dense, whole key range) stop after the int8 MFMAs: they
+// store each tile's int32 scores S = Q8 K8^T into `out` (int32 [B,H,Sq,Sk])
+// through the same copies, LDS layout, MFMA and seeded accumulators, and
+// skip V, the key terms and the softmax. They exist to check those scores
+// bit for bit.
+template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
   constexpr int KC = D / 32;                     // int8 MFMA k-steps / 32-channel blocks
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   constexpr int KI = K_BYTES / 1024, VI = V_BYTES / 1024;   // 1 KB copy instructions per tile
   constexpr int KI_W = KI / NW, VI_W = VI / NW;            // ... per wave
   constexpr int K_ROWS_I = 1024 / D, V_ROWS_I = 1024 / (2 * D);   // rows per copy instruction
-  constexpr int N_COPY_W = KI_W + VI_W;                    // copy instructions per wave per tile
+  constexpr int N_COPY_W = KI_W + (DUMP ? 0 : VI_W);      // copy instructions per wave per tile
   static_assert(KI % NW == 0 && VI % NW == 0, "copy split");
   typedef typename std::conditional<VT == BF16, v8bf, v8h>::type pvec;
 
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // row factor of the log2-domain logits; kept above zero so that an
   // excluded key (-inf) stays -inf when scaled (a zero row's logits are 0
   // either way)
-  const float crow = fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f);
+  const float crow = DUMP ? 1.0f : fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f);
 
   // ---- per-(b,h) sources; every copy and load is range-checked ----
   const unsigned char* kbase = (const unsigned char*)(a.k8 + (int64_t)bh * a.Sk * D);
@@ -415,6 +421,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     for (int i = 0; i < KI_W; ++i) lds_copy<16>(lds_addr(&kbuf[stage][(wave + i * NW) * 1024]), k_src[i], d);
   };
   auto copy_v = [&](int stage, int tile, bool valid) __attribute__((always_inline)) {
+    if constexpr (DUMP) return;
     const int key0 = tile * BN;
     const v4u d = buf_desc(vbase + (int64_t)key0 * v_row, valid ? v_total - (int64_t)key0 * v_row : 0);
 #pragma unroll
@@ -424,6 +431,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // key0 + lane, wave 1 the bias values (range [lo, hi): keys outside it
   // read zero and are excluded when the terms are derived)
   auto copy_terms = [&](int stage, int tile, int lo, int hi, bool valid) __attribute__((always_inline)) {
+    if constexpr (DUMP) return;
     const int nk = valid ? hi - lo : 0;
     const int rel = tile * BN + lane - lo;   // negative offsets wrap and read as out of range
     if (wave == 0) {
@@ -437,6 +445,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // derive the terms of a tile from its copied raw values (the calling
   // wave's own copy must have landed)
   auto derive_terms = [&](int stage, int tile, int lo, int hi) __attribute__((always_inline)) {
+    if constexpr (DUMP) return;
     const int key = tile * BN + lane;
     const bool in = key >= lo && key < hi;
     if (wave == 0) {
@@ -510,6 +519,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     if (iter + 3 < n_tiles) get(iter + 3, t3, l3, h3);
     if (iter + 2 < n_tiles) get(iter + 2, t2, l2, h2);
     copy_terms(st2, t2, l2, h2, iter + 2 < n_tiles);
+
+    if constexpr (DUMP) {
+      // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier
+      int tile, lo, hi;
+      get(iter, tile, lo, hi);
+      int32_t* srow = (int32_t*)a.out + qrow * a.Sk;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = tile * BN + 32 * blk + 8 * g + 4 * hl + r;
+            if (qvalid && key >= lo && key < hi) srow[key] = s[blk][4 * g + r] - kMagicBits;
+          }
+        qk_block(st1, blk);
+      }
+      copy_k(iter % 3, t3, iter + 3 < n_tiles);
+      wait_vmcnt<N_COPY_W>();
+      stage_barrier<N_COPY_W>();
+      return;
+    }
 
     // ===== A: dequantize S(iter); S(iter+1) MFMAs; copies; row max =====
     // unbiased: t = S*ks, crow is applied in the exponent; biased:
@@ -624,7 +655,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // drain this wave's remaining copies (they target stages nobody reads)
   wait_vmcnt<0>();
 
-  store_rows<D, LSE>(a, o, lsum, m_run, b, h, q, qrow, qvalid, hl);
+  if constexpr (!DUMP) store_rows<D, LSE>(a, o, lsum, m_run, b, h, q, qrow, qvalid, hl);
 }
 
 
@@ -649,10 +680,17 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-}  // namespace
+template <int D>
+hipError_t launch_qk_dump_d(const AttnArgs& a, hipStream_t s) {
+  const int qtiles = (a.Sq + 127) / 128;
+  const int total = qtiles * a.B * a.H;
+  if (total == 0) return hipSuccess;
+  attn_fwd_kernel<D, BF16, 4, false, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+  return hipGetLastError();
+}
 
-hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
-  AttnArgs a = args;
+// Derived segment tables of a dense call (up to 4 key segments).
+void derive_segments(AttnArgs& a) {
   int cum = 0;
   for (int g = 0; g < 4; ++g) {
     const bool live = g < a.nseg && a.seg_hi[g] > a.seg_lo[g];
@@ -661,6 +699,19 @@ hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
     if (live) cum += (a.seg_hi[g] + BN - 1) / BN - a.seg_lo[g] / BN;
   }
   a.seg_ntiles = cum;
+}
+
+}  // namespace
+
+hipError_t launch_qk_scores(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  derive_segments(a);
+  return a.D == 128 ? launch_qk_dump_d<128>(a, s) : launch_qk_dump_d<64>(a, s);
+}
+
+hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  derive_segments(a);
   if (a.D == 128) return a.v_dtype == BF16 ? launch_d_vt<128, BF16>(a, s) : launch_d_vt<128, FP16>(a, s);
   return a.v_dtype == BF16 ? launch_d_vt<64, BF16>(a, s) : launch_d_vt<64, FP16>(a, s);
 }

@@ -76,6 +76,9 @@ struct AttnArgs {
   float* lse;           // nullable
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+// int32 scores of the attention kernel's QK stage into a.out (int32 [B,H,Sq,Sk]);
+// uses q8, k8, sizes and one segment [0, Sk).
+hipError_t launch_qk_scores(const AttnArgs& a, hipStream_t s);
 
 struct MergeArgs {
   int64_t B, H, S, D;

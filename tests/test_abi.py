@@ -120,6 +120,16 @@ def test_blockmask_rejects_bad_arguments():
     assert L.qfa_blockmask_to_index(FAKE, 0, 1, 4, 4, FAKE, FAKE, None) == _lib.QFA_OK  # empty: nothing to do
 
 
+def test_qk_scores_rejects_bad_arguments():
+    L = _lib.lib()
+    assert L.qfa_qk_scores_i32(1, 1, 64, 64, 96, FAKE, FAKE, FAKE, None) == _lib.QFA_ERR_UNSUPPORTED
+    assert L.qfa_qk_scores_i32(1, 1, 64, 64, 128, None, FAKE, FAKE, None) == _lib.QFA_ERR_INVALID_ARG
+    assert L.qfa_qk_scores_i32(1, 1, 64, 64, 128, FAKE, FAKE, ctypes.c_void_p(0x10004), None) == \
+        _lib.QFA_ERR_INVALID_ARG                                  # misaligned output
+    assert L.qfa_qk_scores_i32(1, 1, -1, 64, 128, FAKE, FAKE, FAKE, None) == _lib.QFA_ERR_INVALID_ARG
+    assert L.qfa_qk_scores_i32(1, 1, 64, 0, 128, FAKE, FAKE, FAKE, None) == _lib.QFA_OK  # no keys: no scores
+
+
 def test_python_binding_refuses_grad_and_bad_bias():
     import torch
     q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16, requires_grad=True)

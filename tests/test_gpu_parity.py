@@ -38,6 +38,50 @@ def assert_quant_equal(g, ref, center=True):
         assert np.max(np.abs(qm - ref["qmu"])) <= 1e-4 * max(1.0, np.abs(ref["qmu"]).max())
 
 
+# ------------------------------------------------------------ int32 scores --
+
+SCORE_CASES = {
+    "tiny": dict(w="tiny"),
+    "dense_ragged": dict(w="dense4k", H=2, Sq=333, Sk=515),
+    "d64_fp16": dict(w="d64", B=2, H=1, Sq=130, Sk=200),
+    "band_head": dict(w="band", H=1, Sq=257, Sk=33600),
+}
+
+
+@pytest.mark.parametrize("case", list(SCORE_CASES))
+def test_qk_scores_bit_exact(case):
+    """The attention kernel's int8 MFMA scores equal the oracle's int32 dot products bit for bit."""
+    c = dict(SCORE_CASES[case])
+    w = W.WORKLOADS[c.pop("w")]
+    q, k, _ = W.make_qkv(w, **c)
+    ref = oracle.quantize_qk(q, k)
+    s32 = down(qfa.qk_scores_i32(up(ref["q8"]), up(ref["k8"])))
+    B, H = ref["q8"].shape[:2]
+    for b in range(B):
+        for h in range(H):
+            exp = oracle.scores_i32(ref["q8"][b, h], ref["k8"][b, h])
+            got = s32[b, h]
+            if not np.array_equal(got, exp):
+                bad = np.argwhere(got != exp)
+                raise AssertionError(f"(b,h)=({b},{h}): {len(bad)} mismatches, first {bad[0].tolist()}: "
+                                     f"gpu {got[tuple(bad[0])]} oracle {exp[tuple(bad[0])]}")
+
+
+def test_qk_scores_extremes():
+    """All-(+127) and all-(-127) codes reach the largest |S| = D*127^2 exactly; zero rows give 0."""
+    D = 128
+    q8 = np.zeros((1, 1, 96, D), np.int8)
+    k8 = np.zeros((1, 1, 130, D), np.int8)
+    q8[0, 0, :32] = 127
+    q8[0, 0, 32:64] = -127
+    k8[0, 0, :70] = 127
+    k8[0, 0, 70:129] = -127
+    s32 = down(qfa.qk_scores_i32(up(q8), up(k8)))[0, 0]
+    assert np.array_equal(s32, oracle.scores_i32(q8[0, 0], k8[0, 0]))
+    assert s32.max() == D * 127 * 127 and s32.min() == -D * 127 * 127
+    assert (s32[64:] == 0).all() and (s32[:, 129] == 0).all()
+
+
 # ---------------------------------------------------------------- quantize --
 
 QUANT_CASES = {
