@@ -145,7 +145,8 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  *           LSE (pass it whenever K was centred and the LSE is requested).
  * k8, ks:   int8 [B,H,Sk,D], fp32 [B,H,Sk].
  * v:        [B,H,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
- *           v_sh, v_ss); base and row strides 16-byte aligned.
+ *           v_sh, v_ss); base and row strides 16-byte aligned; v_ss below
+ *           2^24 elements (else QFA_ERR_UNSUPPORTED).
  * sm_scale: softmax scale (typically D^-0.5).
  * bias:     nullable additive per-key bias of bias_dtype (QFA_FP32, QFA_BF16
  *           or QFA_FP16), element (b,h,j) at bias + b*bias_sb + h*bias_sh + j;

@@ -173,6 +173,9 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
     if (!k8 || !ks) return fail(QFA_ERR_INVALID_ARG, "k8/ks is NULL");
     if (!aligned16(k8)) return fail(QFA_ERR_INVALID_ARG, "k8 must be 16-byte aligned");
     if ((st = check_view("v", v, v_dtype, v_sb, v_sh, v_ss))) return st;
+    // one 64-key tile of V then spans less than 2^31 bytes (32-bit copy ranges)
+    if (v_ss >= (1ll << 24))
+      return fail(QFA_ERR_UNSUPPORTED, "V sequence stride %lld elements (supported: below 2^24)", (long long)v_ss);
   }
   if (out_dtype != QFA_BF16 && out_dtype != QFA_FP16 && out_dtype != QFA_FP32)
     return fail(QFA_ERR_INVALID_ARG, "out dtype %d", out_dtype);

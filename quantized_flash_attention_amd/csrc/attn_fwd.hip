@@ -83,37 +83,22 @@ __device__ __forceinline__ float load_bias(const void* p, int dtype, int64_t idx
   return dtype == BF16 ? bf16_bits_to_float(h) : half_bits_to_float(h);
 }
 
-// Key tile `it` of a call and the key range [lo, hi) attended inside it
-// (absolute keys, inside [0, Sk)). Dense calls walk the tiles covering up to
-// 4 key segments in order; block-sparse calls walk the query tile's list,
-// where a listed tile outside [0, ntk) counts as an empty tile. Everything
-// here is wave-uniform and lives in SGPRs.
-template <bool SPARSE>
-__device__ __forceinline__ void tile_at(const AttnArgs& a, const int32_t* list, int ntk, int it, int& tile,
-                                        int& lo, int& hi) {
-  if constexpr (SPARSE) {
-    tile = __builtin_amdgcn_readfirstlane(list[it]);
-    if (tile < 0 || tile >= ntk) {
-      tile = 0;
-      lo = hi = 0;
-      return;
-    }
-    lo = tile * BN;
-    hi = lo + (a.vbs ? min(max(__builtin_amdgcn_readfirstlane(a.vbs[tile]), 0), BN) : BN);
-  } else {
-    int t0 = a.seg_t0[0], slo = a.seg_lo[0], shi = a.seg_hi[0], base = 0;
+// Dense calls walk the key tiles that cover up to 4 key segments, segment
+// after segment. Tile `it` of that walk and the bounds [slo, shi) of its
+// segment; everything here is wave-uniform and lives in SGPRs.
+__device__ __forceinline__ void seg_at(const AttnArgs& a, int it, int& tile, int& slo, int& shi) {
+  int t0 = a.seg_t0[0], base = 0;
+  slo = a.seg_lo[0];
+  shi = a.seg_hi[0];
 #pragma unroll
-    for (int g = 1; g < 4; ++g) {
-      const bool past = it >= a.seg_cum[g];
-      t0 = past ? a.seg_t0[g] : t0;
-      slo = past ? a.seg_lo[g] : slo;
-      shi = past ? a.seg_hi[g] : shi;
-      base = past ? a.seg_cum[g] : base;
-    }
-    tile = t0 + it - base;
-    lo = max(slo, tile * BN);
-    hi = min(shi, tile * BN + BN);
+  for (int g = 1; g < 4; ++g) {
+    const bool past = it >= a.seg_cum[g];
+    t0 = past ? a.seg_t0[g] : t0;
+    slo = past ? a.seg_lo[g] : slo;
+    shi = past ? a.seg_hi[g] : shi;
+    base = past ? a.seg_cum[g] : base;
   }
+  tile = t0 + it - base;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -185,6 +170,17 @@ __device__ __forceinline__ v4u buf_desc(const void* base, int64_t bytes) {
   const uint64_t p = (uint64_t)base;
   const unsigned n = bytes <= 0 ? 0u : (bytes >= 0x7fffffff ? 0x7fffffffu : (unsigned)bytes);
   return v4u{(unsigned)p, (unsigned)(p >> 32) & 0xffffu, n, 0x00020000u};
+}
+
+// Same for a size known to be below 2^31 bytes: no clamping, so the
+// descriptor costs a handful of scalar instructions.
+// The values are wave-uniform; readfirstlane states it for the compiler,
+// which otherwise may keep a copy of them in VGPRs.
+__device__ __forceinline__ v4u buf_desc32(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)base;
+  return v4u{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)p),
+             (unsigned)__builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu)),
+             (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
 }
 
 // LDS byte address of a shared-memory location.
@@ -359,19 +355,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     n_tiles = a.seg_ntiles;
   }
   const __attribute__((address_space(4))) int32_t* vbs = (const __attribute__((address_space(4))) int32_t*)a.vbs;
-  // key tile i of this block and the key range [lo, hi) attended inside it
-  auto get = [&](int i, int& tile, int& lo, int& hi) __attribute__((always_inline)) {
+  // The key tiles of this block in loop order, one per call: the tile, the
+  // key range [lo, hi) attended inside it, and whether the walk has not yet
+  // ended (past its end the tile is empty). Dense calls step a cursor and
+  // read the segment tables only when a segment ends; block-sparse calls
+  // read the query tile's list, where an entry outside [0, ntk) is an empty
+  // tile. Wave-uniform throughout.
+  int cur_it = -1, cur_tile = -1, cur_slo = 0, cur_shi = 0;
+  auto next_tile = [&](int& tile, int& lo, int& hi, int& valid) __attribute__((always_inline)) {
+    ++cur_it;
+    valid = cur_it < n_tiles ? 1 : 0;
     if constexpr (SPARSE) {
-      tile = list[i];
-      if (tile < 0 || tile >= ntk) {
-        tile = 0;
-        lo = hi = 0;
-        return;
+      tile = 0;
+      lo = hi = 0;
+      if (valid) {
+        const int t = list[cur_it];
+        if (t >= 0 && t < ntk) {
+          tile = t;
+          lo = t * BN;
+          hi = lo + (vbs ? min(max(vbs[t], 0), BN) : BN);
+        }
       }
-      lo = tile * BN;
-      hi = lo + (vbs ? min(max(vbs[tile], 0), BN) : BN);
     } else {
-      tile_at<false>(a, nullptr, 0, i, tile, lo, hi);
+      ++cur_tile;
+      if (cur_tile * BN >= cur_shi) seg_at(a, cur_it, cur_tile, cur_slo, cur_shi);
+      tile = cur_tile;
+      lo = max(cur_slo, cur_tile * BN);
+      hi = valid ? min(cur_shi, cur_tile * BN + BN) : lo;
     }
   };
 
@@ -389,10 +399,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 
   // ---- per-(b,h) sources; every copy and load is range-checked ----
   const unsigned char* kbase = (const unsigned char*)(a.k8 + (int64_t)bh * a.Sk * D);
-  const int64_t k_total = (int64_t)a.Sk * D;
   const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * 2;
-  const int64_t v_total = a.Sk > 0 ? ((int64_t)(a.Sk - 1) * a.v_ss + D) * 2 : 0;
-  const int v_row = (int)(a.v_ss * 2);
+  const int v_row = (int)(a.v_ss * 2);   // below 2^25 (checked by the caller)
   const float* ksbase = a.ks + (int64_t)bh * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
@@ -413,31 +421,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     v_src[i] = row * v_row + v_chunk_pos<D>(row, pos) * 16;
   }
 
-  // K8 / V rows of a tile into a stage (zeros when `valid` is false)
-  auto copy_k = [&](int stage, int tile, bool valid) __attribute__((always_inline)) {
+  // K8 / V rows of a tile into a stage (zeros when `valid` is false; rows
+  // past Sk read zero). The descriptor covers the tile's rows only, so its
+  // size is a 32-bit scalar computation.
+  auto copy_k = [&](int stage, int tile, int valid) __attribute__((always_inline)) {
     const int key0 = tile * BN;
-    const v4u d = buf_desc(kbase + (int64_t)key0 * D, valid ? k_total - (int64_t)key0 * D : 0);
+    const int rows = valid ? min(BN, a.Sk - key0) : 0;
+    const v4u d = buf_desc32(kbase + (int64_t)key0 * D, rows * D);
 #pragma unroll
     for (int i = 0; i < KI_W; ++i) lds_copy<16>(lds_addr(&kbuf[stage][(wave + i * NW) * 1024]), k_src[i], d);
   };
-  auto copy_v = [&](int stage, int tile, bool valid) __attribute__((always_inline)) {
+  auto copy_v = [&](int stage, int tile, int valid) __attribute__((always_inline)) {
     if constexpr (DUMP) return;
     const int key0 = tile * BN;
-    const v4u d = buf_desc(vbase + (int64_t)key0 * v_row, valid ? v_total - (int64_t)key0 * v_row : 0);
+    const int rows = valid ? min(BN, a.Sk - key0) : 0;
+    const v4u d = buf_desc32(vbase + (int64_t)key0 * v_row, rows > 0 ? (rows - 1) * v_row + 2 * D : 0);
 #pragma unroll
     for (int i = 0; i < VI_W; ++i) lds_copy<16>(lds_addr(&vbuf[stage][(wave + i * NW) * 1024]), v_src[i], d);
   };
   // raw key terms of a tile: wave 0 copies the key scales of keys
   // key0 + lane, wave 1 the bias values (range [lo, hi): keys outside it
   // read zero and are excluded when the terms are derived)
-  auto copy_terms = [&](int stage, int tile, int lo, int hi, bool valid) __attribute__((always_inline)) {
+  auto copy_terms = [&](int stage, int tile, int lo, int hi, int valid) __attribute__((always_inline)) {
     if constexpr (DUMP) return;
     const int nk = valid ? hi - lo : 0;
     const int rel = tile * BN + lane - lo;   // negative offsets wrap and read as out of range
     if (wave == 0) {
-      lds_copy<4>(lds_addr(&kt[stage].raw[0][0]), rel * 4, buf_desc(ksbase + lo, (int64_t)nk * 4));
+      lds_copy<4>(lds_addr(&kt[stage].raw[0][0]), rel * 4, buf_desc32(ksbase + lo, nk * 4));
     } else if (HAS_BIAS && wave == 1) {
-      const v4u d = buf_desc((const unsigned char*)a.bias + (bias_off + lo) * bias_esz, (int64_t)nk * bias_esz);
+      const v4u d = buf_desc32((const unsigned char*)a.bias + (bias_off + lo) * bias_esz, nk * bias_esz);
       if (bias_esz == 4) lds_copy<4>(lds_addr(&kt[stage].raw[1][0]), rel * 4, d);
       else lds_copy<2>(lds_addr(&kt[stage].raw[1][0]), rel * 2, d);
     }
@@ -487,15 +499,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   };
 
   // ---- prologue: K(0), K(1), V(0) and the terms of tiles 0, 1 in LDS; S(0) ----
+  int t2, l2, h2, v2;   // tile iter+2 of the loop below (v2: inside the walk)
   {
-    int t0 = 0, l0 = 0, h0 = 0, t1 = 0, l1 = 0, h1 = 0;
-    if (n_tiles > 0) get(0, t0, l0, h0);
-    if (n_tiles > 1) get(1, t1, l1, h1);
-    copy_terms(0, t0, l0, h0, n_tiles > 0);
-    copy_terms(1, t1, l1, h1, n_tiles > 1);
-    copy_k(0, t0, n_tiles > 0);
-    copy_v(0, t0, n_tiles > 0);
-    copy_k(1, t1, n_tiles > 1);
+    int t0, l0, h0, v0, t1, l1, h1, v1;
+    next_tile(t0, l0, h0, v0);
+    next_tile(t1, l1, h1, v1);
+    copy_terms(0, t0, l0, h0, v0);
+    copy_terms(1, t1, l1, h1, v1);
+    copy_k(0, t0, v0);
+    copy_v(0, t0, v0);
+    copy_k(1, t1, v1);
     wait_vmcnt<0>();
     derive_terms(0, t0, l0, h0);
     derive_terms(1, t1, l1, h1);
@@ -504,10 +517,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     qk_block(0, 1);
     // every wave's reads of K(0) are done before stage 0 is refilled
     stage_barrier<0>();
-    int t2 = 0, l2 = 0, h2 = 0;
-    if (n_tiles > 2) get(2, t2, l2, h2);
-    copy_k(2, t2, n_tiles > 2);
-    copy_v(1, t1, n_tiles > 1);
+    next_tile(t2, l2, h2, v2);
+    copy_k(2, t2, v2);
+    copy_v(1, t1, v1);
   }
 
   // One tile. Excluded keys (segment edges, pad keys of block-sparse tiles)
@@ -515,15 +527,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   auto tile_body = [&](int iter, int st0, int st1, int st2) __attribute__((always_inline)) {
     // st0 = iter % 3, st1 = (iter + 1) % 3, st2 = (iter + 2) % 3
     const KeyTerms& tc = kt[st0];
-    int t3 = 0, l3 = 0, h3 = 0, t2 = 0, l2 = 0, h2 = 0;
-    if (iter + 3 < n_tiles) get(iter + 3, t3, l3, h3);
-    if (iter + 2 < n_tiles) get(iter + 2, t2, l2, h2);
-    copy_terms(st2, t2, l2, h2, iter + 2 < n_tiles);
+    int t3, l3, h3, v3;
+    next_tile(t3, l3, h3, v3);
+    copy_terms(st2, t2, l2, h2, v2);
 
     if constexpr (DUMP) {
-      // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier
-      int tile, lo, hi;
-      get(iter, tile, lo, hi);
+      // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier;
+      // the walk of a score dump is the single segment [0, Sk)
+      const int tile = iter, lo = iter * BN, hi = min(a.Sk, lo + BN);
       int32_t* srow = (int32_t*)a.out + qrow * a.Sk;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -536,9 +547,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
           }
         qk_block(st1, blk);
       }
-      copy_k(iter % 3, t3, iter + 3 < n_tiles);
+      copy_k(iter % 3, t3, v3);
       wait_vmcnt<N_COPY_W>();
       stage_barrier<N_COPY_W>();
+      t2 = t3;
+      v2 = v3;
       return;
     }
 
@@ -565,9 +578,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
         }
       }
       qk_block(st1, blk);   // the score registers of this block are free again
-      if (blk == 0) copy_k(iter % 3, t3, iter + 3 < n_tiles);   // K(iter+3) over K(iter)
+      if (blk == 0) copy_k(iter % 3, t3, v3);   // K(iter+3) over K(iter)
     }
-    copy_v(st2, t2, iter + 2 < n_tiles);                        // V(iter+2) over V(iter-1)
+    copy_v(st2, t2, v2);                        // V(iter+2) over V(iter-1)
     // crow > 0, so max(u)*crow = max(u*crow) (also for -inf)
     const float mx = (HAS_BIAS) ? xmax32(max32(t)) : xmax32(max32(t)) * crow;
 
@@ -642,6 +655,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     wait_vmcnt<N_COPY_W>();
     derive_terms(st2, t2, l2, h2);
     stage_barrier<N_COPY_W>();
+    t2 = t3;
+    l2 = l3;
+    h2 = h3;
+    v2 = v3;
   };
 
   int st0 = 0, st1 = 1, st2 = 2;
