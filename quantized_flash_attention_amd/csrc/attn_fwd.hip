@@ -299,14 +299,16 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 //
 // Software pipeline, per 64-key tile j (one barrier per tile). LDS holds
 // three stages of K8, V and key terms; at the start of iteration j, K(j+1),
-// V(j) and the terms of tiles j, j+1 are in LDS, S(j) is in registers, and
-// the copies of K(j+2) and V(j+1) are in flight.
+// V(j), the key terms of tile j and the raw terms of tile j+1 are in LDS,
+// S(j) is in registers, and the copies of K(j+2) and V(j+1) are in flight.
 //   A  dequantize S(j) while the int8 MFMAs of S(j+1) = K8(j+1) Q8^T run;
-//      start the copies of K(j+3) and V(j+2); row max; lazy rescale.
+//      start the copies of K(j+3), V(j+2) and the raw terms of tile j+2;
+//      write the key terms of tile j+1 (raw values copied during tile
+//      j-1); row max; lazy rescale.
 //   B  p = exp2(t - m) one 16-key chunk at a time, packed to V's type, row
 //      sum, and the bf16 MFMAs O^T += V^T P^T of that chunk.
-//   C  write the key terms of tile j+2 (fetched during the tile); wait for
-//      this wave's copies of K(j+2) and V(j+1); barrier.
+//   C  wait for this wave's copies of K(j+2), V(j+1) and the raw terms of
+//      tile j+2; barrier.
 // Copies past the end of the tile list use empty buffer ranges and write
 // zeros, and the MFMAs of a tile past the end run on those zeros, so the
 // loop body has no branch besides the rescale.
@@ -498,10 +500,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     }
   };
 
-  // ---- prologue: K(0), K(1), V(0) and the terms of tiles 0, 1 in LDS; S(0) ----
-  int t2, l2, h2, v2;   // tile iter+2 of the loop below (v2: inside the walk)
+  // ---- prologue: K(0), K(1), V(0), the terms of tile 0 and the raw terms of
+  // tile 1 in LDS; S(0) ----
+  int t1, l1, h1, v1;   // tiles iter+1 and iter+2 of the loop below
+  int t2, l2, h2, v2;   // (v: inside the walk)
   {
-    int t0, l0, h0, v0, t1, l1, h1, v1;
+    int t0, l0, h0, v0;
     next_tile(t0, l0, h0, v0);
     next_tile(t1, l1, h1, v1);
     copy_terms(0, t0, l0, h0, v0);
@@ -511,7 +515,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_k(1, t1, v1);
     wait_vmcnt<0>();
     derive_terms(0, t0, l0, h0);
-    derive_terms(1, t1, l1, h1);
     stage_barrier<0>();
     qk_block(0, 0);
     qk_block(0, 1);
@@ -530,6 +533,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     int t3, l3, h3, v3;
     next_tile(t3, l3, h3, v3);
     copy_terms(st2, t2, l2, h2, v2);
+    // terms of tile iter+1 from the raw values copied during the previous
+    // tile (first read after this tile's barrier)
+    derive_terms(st1, t1, l1, h1);
 
     if constexpr (DUMP) {
       // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier;
@@ -550,6 +556,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       copy_k(iter % 3, t3, v3);
       wait_vmcnt<N_COPY_W>();
       stage_barrier<N_COPY_W>();
+      t1 = t2;
+      v1 = v2;
       t2 = t3;
       v2 = v3;
       return;
@@ -651,10 +659,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     }
 
     // ===== C: this wave's copies older than this tile's K/V copies are done;
-    // terms of tile iter+2; barrier =====
+    // barrier =====
     wait_vmcnt<N_COPY_W>();
-    derive_terms(st2, t2, l2, h2);
     stage_barrier<N_COPY_W>();
+    t1 = t2;
+    l1 = l2;
+    h1 = h2;
+    v1 = v2;
     t2 = t3;
     l2 = l3;
     h2 = h3;
