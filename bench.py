@@ -266,7 +266,7 @@ def main() -> int:
 
 
 COPY_BYTES = 256 << 20
-UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false>"
+UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false, false>"
 
 
 def _counter_per_dispatch(path: str, counter: str):
