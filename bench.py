@@ -71,6 +71,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows of head 0 the oracle computes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step: time the other configurations (dense 4k with LSE off/on, d64 fp16, "
+                         "tile-64 block-sparse 128k) and a bf16 / int8 GEMM on the box; one JSON line each")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE passes over "
                          "this script with --copy-calibration) into " + os.path.relpath(PMC_FILE, ROOT))
@@ -94,6 +97,8 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    if args.configs:
+        return other_configs(dev)
     w = W.WORKLOADS["band"]
     B, H, Sq, Sk, D = w.B, w.H, w.Sq, w.Sk, w.D
     core, skirt = w.extras["core"], w.extras["skirt"]
@@ -248,6 +253,7 @@ def main() -> int:
         "page_context": {"hardware": "RTX 5090 (comfy-kitchen int8_attention)", **PAGE_MS,
                          "step_tflops": round(page_value, 1)},
         "input_gen_s": round(gen_s, 1),
+        "device": device_info(dev),
     }
 
     if args.copy_calibration:
@@ -327,6 +333,126 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> int:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(json.dumps(out["launches"]["unmasked"]))
+    return 0
+
+
+def device_info(dev) -> dict:
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def _time_ms(fn, iters: int, warmup: int = 3) -> float:
+    """Median milliseconds of fn() over `iters` launches, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def other_configs(dev) -> int:
+    """One JSON line per configuration besides the step's banded workload: quantize and attention
+    times, effective TFLOPS (4*B*H*Sq*Sk_eff*D; block-sparse counts the selected 64x64 tile pairs)
+    and the fraction of the blended int8/bf16 MFMA peak; quantize / map-to-index bandwidth against
+    HBM's 8 TB/s. Last, a bf16 and an int8 GEMM through torch as an on-box matrix-core reference."""
+    import numpy as np
+    import torch
+
+    import quantized_flash_attention_amd as qfa
+    import workloads as W
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def qbytes(B, H, Sq, Sk, D, esz):
+        # read Q and K once; write codes, scales, K mean, centring term
+        return B * H * (Sq + Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
+
+    info = device_info(dev)
+    for name in ("dense4k", "d64"):
+        w = W.WORKLOADS[name]
+        q_np, k_np, v_np = W.make_qkv(w)
+        q, k, v = up(q_np), up(k_np), up(v_np)
+        ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
+        qk = qfa.quantize_qk(q, k, workspace=ws)
+        out = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+        t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
+        t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out), 20)
+        t_l = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out, lse=lse), 20)
+        fl = 4.0 * w.B * w.H * w.Sq * w.Sk * w.D
+        qb = qbytes(w.B, w.H, w.Sq, w.Sk, w.D, 2)
+        print(json.dumps({
+            "config": name, "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} {w.dtype}",
+            "quantize_ms": round(t_q, 4), "quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
+            "quantize_frac_hbm": round(qb / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+            "attn_ms": round(t_a, 4), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
+            "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
+            "attn_lse_ms": round(t_l, 4), "lse_over_plain": round(t_l / t_a, 3), "device": info}), flush=True)
+        del q, k, v, qk, out, lse, ws
+        torch.cuda.empty_cache()
+
+    w = W.WORKLOADS["sparse"]
+    T = w.Sk // 64
+    mask_np = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
+    vbs_np = W.sparse_vbs(T, w.extras["last_valid"])
+    q_np, k_np, v_np = W.make_qkv(w)
+    for x in (q_np, k_np, v_np):
+        W.zero_pads(x, vbs_np)
+    q, k, v = up(q_np), up(k_np), up(v_np)
+    del q_np, k_np, v_np
+    mask, vbs, vsc = up(mask_np.astype(np.uint8)), up(vbs_np), up(W.v_scale(w))
+    ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
+    qk = qfa.quantize_qk(q, k, vbs=vbs, workspace=ws)
+    idx, cnt = qfa.blockmask_to_index(mask)
+    out = torch.empty_like(q)
+    t_m = _time_ms(lambda: qfa.blockmask_to_index(mask), 20)
+    t_q = _time_ms(lambda: qfa.quantize_qk(q, k, vbs=vbs, workspace=ws), 10)
+    t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, index=idx, count=cnt, vbs=vbs, v_scale=vsc, out=out), 10)
+    pairs = int(mask_np.sum())
+    fl = 4.0 * w.D * 64 * 64 * pairs
+    mb = mask_np.size + pairs * 4 + w.B * w.H * T * 4   # mask bytes read; entries + counts written
+    qb = qbytes(w.B, w.H, w.Sq, w.Sk, w.D, 2)
+    print(json.dumps({
+        "config": "sparse", "shape": f"B{w.B} H{w.H} S{w.Sq} D{w.D} {w.dtype}, tile-64 mask prefix 8 + band 48",
+        "tile_pairs": pairs, "map_to_index_ms": round(t_m, 4), "map_to_index_GBps": round(mb / (t_m * 1e-3) / 1e9, 1),
+        "quantize_ms": round(t_q, 4), "quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
+        "attn_ms": round(t_a, 4), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
+        "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
+        "end_to_end_ms": round(t_m + t_q + t_a, 4), "device": info}), flush=True)
+    del q, k, v, qk, out, idx, cnt, mask, ws
+    torch.cuda.empty_cache()
+
+    # matrix-core reference through torch (hipBLASLt / rocBLAS): 8192^3 GEMMs
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    t_bf = _time_ms(lambda: torch.matmul(a, b), 10)
+    gemm = {"bf16_tflops": round(2.0 * n ** 3 / (t_bf * 1e-3) / 1e12, 1)}
+    try:
+        a8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+        b8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+        t_i8 = _time_ms(lambda: torch._int_mm(a8, b8), 10)
+        gemm["int8_tops"] = round(2.0 * n ** 3 / (t_i8 * 1e-3) / 1e12, 1)
+    except (RuntimeError, AttributeError) as e:
+        gemm["int8_tops"] = None
+        gemm["int8_note"] = str(e).splitlines()[0][:120]
+    print(json.dumps({"config": "gemm_reference", "m=n=k": n, **gemm,
+                      "published_dense_peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "int8_tops": PEAK_I8_TOPS},
+                      "device": info}), flush=True)
     return 0
 
 
