@@ -155,6 +155,10 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * index, count, vbs: block-sparse mode when index != NULL: int32 [B,H,T,T],
  *           int32 [B,H,T], int32 [T] (from qfa_blockmask_to_index; vbs may be
  *           NULL for full tiles), T = Sq/64 = Sk/64. Not combinable with bias.
+ *           Each row's entries [0, count) must be strictly ascending key tiles
+ *           in [0, T), as qfa_blockmask_to_index writes them (the kernel
+ *           merges the lists of neighbouring query tiles); other lists give
+ *           unspecified results, with every access still in bounds.
  * v_scale:  nullable fp32 [H,D] per-(head,channel) factor applied to O.
  * nseg, seg: host array of nseg (<= 4) (start, length) pairs of key ranges,
  *           ascending and disjoint; nseg = 0 means the whole [0, Sk).

@@ -11,8 +11,9 @@
 // writer per row).
 //
 // Work decomposition
-//   block  = BM = 32*NW query rows of one (b,h); NW = 4 dense, 2 block-sparse
-//            (a 64-query tile, the unit of the tile mask).
+//   block  = BM = 128 query rows of one (b,h), 4 waves. Block-sparse blocks
+//            hold two 64-query tiles (the unit of the tile mask) and walk
+//            the union of their key-tile lists.
 //   wave   = 32 query rows. The wave computes S^T = K8 Q8^T with
 //            v_mfma_i32_32x32x32_i8 (A = K rows from LDS, B = Q codes kept in
 //            VGPRs for the whole key loop), so each lane ends up owning one
@@ -217,9 +218,10 @@ __device__ __forceinline__ void lds_copy(unsigned lds, int voff, v4u desc) {
 // Per-key terms of one tile: sc[0] key scale ks, sc[1] = -kMagic*ks (turns
 // the biased accumulator into S*ks with one FMA; for an excluded key ks = 0
 // and sc[1] = -inf, so its score comes out -inf), sc[2] log2-domain bias
-// term bias*log2(e) (biased calls only), sc[3] unused. Wave 0 copies the key
-// scales into raw[0] and derives sc[0], sc[1]; wave 1 copies the bias
-// values into raw[1] and derives sc[2].
+// term bias*log2(e) (biased calls only), sc[3] the -kMagic*ks / -inf terms
+// of the second query tile of a block-sparse block. Wave 0 copies the key
+// scales into raw[0] and derives sc[0], sc[1] (and sc[3]); wave 1 copies the
+// bias values into raw[1] and derives sc[2].
 struct KeyTerms {
   float sc[4][BN];
   uint32_t raw[2][BN];
@@ -341,44 +343,63 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int hl = lane / 32;          // k-group of this lane in the MFMA operands
+  // key-term row of this wave's additive terms (block-sparse: per query tile)
+  const int nks_row = (SPARSE && wave >= 2) ? 3 : 1;
   const int q = qt * BM + wave * 32 + (lane % 32);
   const bool qvalid = q < a.Sq;
   const int64_t qrow = (int64_t)bh * a.Sq + q;
 
-  // ---- tile list (scalar loads: the lists are read-only here) ----
-  const __attribute__((address_space(4))) int32_t* list = nullptr;
-  int ntk = 0, n_tiles;
+  // ---- tile lists (scalar loads: the lists are read-only here) ----
+  // A block-sparse block covers the query tiles 2qt (waves 0, 1) and 2qt+1
+  // (waves 2, 3) and walks the union of their key-tile lists, so the two
+  // share every K8/V copy; a tile only one of them attends carries -inf
+  // terms for the other.
+  const __attribute__((address_space(4))) int32_t* list_a = nullptr;
+  const __attribute__((address_space(4))) int32_t* list_b = nullptr;
+  int ntk = 0, n_tiles, na = 0, nb = 0, ia = 0, ib = 0;
   if constexpr (SPARSE) {
     ntk = a.Sk / BN;
-    list = (const __attribute__((address_space(4))) int32_t*)(a.index + ((int64_t)bh * ntk + qt) * ntk);
-    const int cnt = ((const __attribute__((address_space(4))) int32_t*)a.count)[(int64_t)bh * ntk + qt];
-    n_tiles = min(max(cnt, 0), ntk);
+    const int qa = 2 * qt, qb = 2 * qt + 1;
+    const __attribute__((address_space(4))) int32_t* cnt = (const __attribute__((address_space(4))) int32_t*)a.count;
+    list_a = (const __attribute__((address_space(4))) int32_t*)(a.index + ((int64_t)bh * ntk + qa) * ntk);
+    list_b = qb < ntk ? list_a + ntk : list_a;
+    na = min(max(cnt[(int64_t)bh * ntk + qa], 0), ntk);
+    nb = qb < ntk ? min(max(cnt[(int64_t)bh * ntk + qb], 0), ntk) : 0;
+    n_tiles = INT32_MAX;   // the length of the union, known once the walk reaches its end
   } else {
     n_tiles = a.seg_ntiles;
   }
   const __attribute__((address_space(4))) int32_t* vbs = (const __attribute__((address_space(4))) int32_t*)a.vbs;
   // The key tiles of this block in loop order, one per call: the tile, the
-  // key range [lo, hi) attended inside it, and whether the walk has not yet
-  // ended (past its end the tile is empty). Dense calls step a cursor and
-  // read the segment tables only when a segment ends; block-sparse calls
-  // read the query tile's list, where an entry outside [0, ntk) is an empty
-  // tile. Wave-uniform throughout.
+  // key range [lo, hi) attended inside it, and `valid`: 0 past the end of
+  // the walk, else bit 0 set, plus (block-sparse) bit 1 when query tile 2qt
+  // attends it and bit 2 when 2qt+1 does. Dense calls step a cursor and read
+  // the segment tables only when a segment ends. Block-sparse calls merge
+  // the two ascending lists (entries are clamped into [0, ntk); lists that
+  // are not strictly ascending give unspecified results but stay in bounds,
+  // and the walk ends after at most na + nb steps). Wave-uniform throughout.
   int cur_it = -1, cur_tile = -1, cur_slo = 0, cur_shi = 0;
   auto next_tile = [&](int& tile, int& lo, int& hi, int& valid) __attribute__((always_inline)) {
     ++cur_it;
-    valid = cur_it < n_tiles ? 1 : 0;
     if constexpr (SPARSE) {
-      tile = 0;
-      lo = hi = 0;
-      if (valid) {
-        const int t = list[cur_it];
-        if (t >= 0 && t < ntk) {
-          tile = t;
-          lo = t * BN;
-          hi = lo + (vbs ? min(max(vbs[t], 0), BN) : BN);
-        }
+      const int ta = ia < na ? min(max(list_a[ia], 0), ntk - 1) : INT32_MAX;
+      const int tb = ib < nb ? min(max(list_b[ib], 0), ntk - 1) : INT32_MAX;
+      const int t = min(ta, tb);
+      if (t == INT32_MAX) {
+        n_tiles = min(n_tiles, cur_it);
+        tile = 0;
+        lo = hi = 0;
+        valid = 0;
+      } else {
+        valid = 1 | (ta == t ? 2 : 0) | (tb == t ? 4 : 0);
+        ia += ta == t ? 1 : 0;
+        ib += tb == t ? 1 : 0;
+        tile = t;
+        lo = t * BN;
+        hi = lo + (vbs ? min(max(vbs[t], 0), BN) : BN);
       }
     } else {
+      valid = cur_it < n_tiles ? 1 : 0;
       ++cur_tile;
       if (cur_tile * BN >= cur_shi) seg_at(a, cur_it, cur_tile, cur_slo, cur_shi);
       tile = cur_tile;
@@ -458,7 +479,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   };
   // derive the terms of a tile from its copied raw values (the calling
   // wave's own copy must have landed)
-  auto derive_terms = [&](int stage, int tile, int lo, int hi) __attribute__((always_inline)) {
+  // (block-sparse: sc[1] holds the terms of query tile 2qt, sc[3] those of
+  // 2qt+1, which differ in the tiles only one of them attends)
+  auto derive_terms = [&](int stage, int tile, int lo, int hi, int flags) __attribute__((always_inline)) {
     if constexpr (DUMP) return;
     const int key = tile * BN + lane;
     const bool in = key >= lo && key < hi;
@@ -466,7 +489,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       const float ks = in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f;
       kt[stage].sc[0][lane] = ks;
       // an excluded key dequantizes to fma(x, 0, -inf) = -inf
-      kt[stage].sc[1][lane] = in ? -kMagic * ks : -INFINITY;
+      const bool in_a = in && (!SPARSE || (flags & 2));
+      kt[stage].sc[1][lane] = in_a ? -kMagic * ks : -INFINITY;
+      if (SPARSE) kt[stage].sc[3][lane] = in && (flags & 4) ? -kMagic * ks : -INFINITY;
     } else if (HAS_BIAS && wave == 1) {
       const uint32_t r = kt[stage].raw[1][lane];
       const float bias = a.bias_dtype == FP32 ? __uint_as_float(r)
@@ -514,7 +539,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_v(0, t0, v0);
     copy_k(1, t1, v1);
     wait_vmcnt<0>();
-    derive_terms(0, t0, l0, h0);
+    derive_terms(0, t0, l0, h0, v0);
     stage_barrier<0>();
     qk_block(0, 0);
     qk_block(0, 1);
@@ -535,7 +560,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_terms(st2, t2, l2, h2, v2);
     // terms of tile iter+1 from the raw values copied during the previous
     // tile (first read after this tile's barrier)
-    derive_terms(st1, t1, l1, h1);
+    derive_terms(st1, t1, l1, h1, v1);
 
     if constexpr (DUMP) {
       // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier;
@@ -573,7 +598,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       for (int g = 0; g < 4; ++g) {
         const int kk = 32 * blk + 8 * g + 4 * hl;
         const float4 kv = *(const float4*)(&tc.sc[0][kk]);
-        const float4 nv = *(const float4*)(&tc.sc[1][kk]);
+        const float4 nv = *(const float4*)(&tc.sc[nks_row][kk]);
         const float kvs[4] = {kv.x, kv.y, kv.z, kv.w};
         const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
 #pragma unroll
@@ -690,14 +715,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 template <int D, int VT>
 hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   const bool sparse = a.index != nullptr;
-  const int NW = sparse ? 2 : 4;
-  const int BM = 32 * NW;
-  const int qtiles = (a.Sq + BM - 1) / BM;
+  const int qtiles = (a.Sq + 127) / 128;   // 128 query rows (two 64-query tiles) per block
   const int total = qtiles * a.B * a.H;
   if (total == 0) return hipSuccess;
   if (sparse) {
-    if (a.lse) attn_fwd_kernel<D, VT, 2, true, false, true><<<total, 128, 0, s>>>(a, qtiles, total);
-    else attn_fwd_kernel<D, VT, 2, true, false, false><<<total, 128, 0, s>>>(a, qtiles, total);
+    if (a.lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, true, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
   } else if (a.bias) {
     if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);

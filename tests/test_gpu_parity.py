@@ -318,6 +318,24 @@ def test_sparse_parity_small():
     check_lse(l, l_ref, what="sparse")
 
 
+def test_sparse_tile_pairs():
+    """Query tiles 2p and 2p+1 share a block that walks the union of their key lists: disjoint
+    lists (every key tile masked for one half), both lists empty, identical lists, and a last
+    block with a single query tile (T odd)."""
+    T, H = 7, 1
+    mask = np.zeros((1, H, T, T), bool)
+    mask[0, 0, 0, 0::2] = True      # tile 0: even key tiles only
+    mask[0, 0, 1, 1::2] = True      # tile 1: odd key tiles only
+    # tiles 2 and 3 attend nothing: O = 0, LSE = -inf for both
+    mask[0, 0, 4, [1, 2, 6]] = True
+    mask[0, 0, 5, [1, 2, 6]] = True
+    mask[0, 0, 6, [0, 3, 5, 6]] = True
+    vbs = np.array([64, 40, 64, 0, 64, 64, 9], np.int32)
+    o, l, o_ref, l_ref = _sparse_case(T, H, mask, vbs)
+    check_o(o, o_ref, what="sparse tile pairs")
+    check_lse(l, l_ref, what="sparse tile pairs")
+
+
 def test_sparse_band_structure():
     T, H = 40, 2
     mask = W.sparse_mask(T, H, prefix=3, band=5)
