@@ -404,3 +404,48 @@ def test_sparse_full_size_sampled():
     o, l, o_ref, l_ref = _sparse_case(T, w.H, mask, vbs, rows=rows)
     check_o(o, o_ref, rows, "sparse full")
     check_lse(l, l_ref, rows, "sparse full")
+
+
+# ------------------------------------------------------------ HIP graph --
+def test_graph_capture_replays():
+    """One step of the path (quantize, unmasked, fp32 bias, core/skirt split with LSE, merge)
+    captured in a HIP graph: every replay, with eager work and synchronisation between replays,
+    reproduces the eager results bit for bit (the library enqueues only kernels: no memset
+    nodes, no allocation, no synchronisation)."""
+    w = W.WORKLOADS["band"]
+    Sk = 1680
+    core, skirt = (336, 1008), 336
+    q, k, v = W.make_qkv(w, H=2, Sq=256, Sk=Sk)
+    bias = W.bias_tensor(W.band_bias(Sk, core=core, skirt=skirt), "fp32")
+    tq, tk, tv, tb = up(q), up(k), up(v), up(bias)
+    ws = torch.empty(qfa.quantize_workspace_bytes(1, 2, Sk, 128), dtype=torch.uint8, device=tq.device)
+
+    def step():
+        qk = qfa.quantize_qk(tq, tk, workspace=ws)
+        o_un = qfa.attn_fwd(qk, tv, w.sm_scale)
+        o_b = qfa.attn_fwd(qk, tv, w.sm_scale, bias=tb)
+        o_c, l_c = qfa.attn_fwd(qk, tv, w.sm_scale, segments=[core], out_dtype=torch.float32, return_lse=True)
+        o_s, l_s = qfa.attn_fwd(qk, tv, w.sm_scale, bias=tb, segments=[(0, skirt), (core[0] + core[1], skirt)],
+                                out_dtype=torch.float32, return_lse=True)
+        o_m, l_m = qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+        return [qk["q8"], qk["k8"], qk["qs"], qk["ks"], qk["kmean"], qk["qmu"], o_un, o_b, o_m, l_m]
+
+    eager = [t.clone() for t in step()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        for t in outs:                       # eager work between replays
+            t.zero_()
+        step()                               # and an eager step on the same inputs
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(outs, eager):
+            assert torch.equal(t, e), f"replay {rep}: a captured output differs from the eager step"
