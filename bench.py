@@ -405,6 +405,25 @@ def other_configs(dev) -> int:
         del q, k, v, qk, out, lse, ws
         torch.cuda.empty_cache()
 
+    # the banded workload with the pages' bool [1,1,1,K] keep mask (raised-cosine weight > 1e-3)
+    w = W.WORKLOADS["band"]
+    q_np, k_np, v_np = W.make_qkv(w)
+    q, k, v = up(q_np), up(k_np), up(v_np)
+    del q_np, k_np, v_np
+    weights = np.exp(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]))
+    keep = torch.from_numpy((weights > 1e-3).reshape(1, 1, 1, -1)).to(dev)
+    ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
+    qk = qfa.quantize_qk(q, k, workspace=ws)
+    out = torch.empty_like(q)
+    t_u = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out), 10)
+    t_k = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=keep, out=out), 10)
+    print(json.dumps({
+        "config": "band_keep_mask", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} {w.dtype}",
+        "kept_keys": int(keep.sum().item()), "unmasked_ms": round(t_u, 4), "keep_mask_ms": round(t_k, 4),
+        "keep_over_unmasked": round(t_k / t_u, 3), "device": info}), flush=True)
+    del q, k, v, qk, out, keep, ws
+    torch.cuda.empty_cache()
+
     w = W.WORKLOADS["sparse"]
     T = w.Sk // 64
     mask_np = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])

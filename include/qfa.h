@@ -55,6 +55,7 @@ extern "C" {
 #define QFA_BF16 1
 #define QFA_FP16 2
 #define QFA_FP32 3
+#define QFA_BOOL 4 /* bytes, nonzero = true (a keep mask) */
 
 #define QFA_MAX_SEGMENTS 4
 
@@ -152,6 +153,11 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  *           or QFA_FP16), element (b,h,j) at bias + b*bias_sb + h*bias_sh + j;
  *           pass 0 for a broadcast batch/head stride. It is shared by every
  *           query row (a [B|1,H|1,1,K] tensor or a stride-0 expansion of one).
+ *           With bias_dtype QFA_BOOL it is a keep mask of the same layout
+ *           (one byte per key, nonzero attends; torch bool semantics): a
+ *           masked key is excluded (-inf), so a row whose keys are all masked
+ *           gets O = 0 and LSE = -inf. The mask is folded into the per-key
+ *           terms and adds no per-score work.
  * index, count, vbs: block-sparse mode when index != NULL: int32 [B,H,T,T],
  *           int32 [B,H,T], int32 [T] (from qfa_blockmask_to_index; vbs may be
  *           NULL for full tiles), T = Sq/64 = Sk/64. Not combinable with bias.

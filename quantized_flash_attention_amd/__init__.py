@@ -21,7 +21,7 @@ import math
 import torch
 
 from . import _lib
-from ._lib import QFA_BF16, QFA_FP16, QFA_FP32, QFAError
+from ._lib import QFA_BF16, QFA_BOOL, QFA_FP16, QFA_FP32, QFAError
 
 __all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
            "quantize_workspace_bytes", "qk_scores_i32"]
@@ -136,7 +136,9 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
     """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
 
     bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
-        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16.
+        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16. A bool
+        tensor of that layout is a keep mask (True attends), applied through
+        the key terms at no per-score cost.
     index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
     segments: up to 4 ascending disjoint (start, length) key ranges.
     return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
@@ -167,7 +169,7 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
             raise NotImplementedError("a materialised per-query bias is not supported; pass [..,1,K] or a stride-0 expansion")
         if bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H):
             raise ValueError("bias batch/head dims must be 1 or match")
-        bdt = _DT.get(bias.dtype)
+        bdt = QFA_BOOL if bias.dtype == torch.bool else _DT.get(bias.dtype)
         if bdt is None:
             raise ValueError(f"bias dtype {bias.dtype}")
         bsb = bias.stride(0) if bias.shape[0] > 1 else 0

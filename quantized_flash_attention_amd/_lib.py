@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqfa.so")
 
 QFA_OK, QFA_ERR_INVALID_ARG, QFA_ERR_UNSUPPORTED, QFA_ERR_HIP = 0, 1, 2, 3
-QFA_BF16, QFA_FP16, QFA_FP32 = 1, 2, 3
+QFA_BF16, QFA_FP16, QFA_FP32, QFA_BOOL = 1, 2, 3, 4
 
 EXPORTS = (
     "qfa_version",

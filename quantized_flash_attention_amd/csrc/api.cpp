@@ -183,7 +183,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(QFA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (v_scale && !aligned16(v_scale)) return fail(QFA_ERR_INVALID_ARG, "v_scale must be 16-byte aligned");
   if (bias) {
-    if (bias_dtype != QFA_FP32 && bias_dtype != QFA_BF16 && bias_dtype != QFA_FP16)
+    if (bias_dtype != QFA_FP32 && bias_dtype != QFA_BF16 && bias_dtype != QFA_FP16 && bias_dtype != QFA_BOOL)
       return fail(QFA_ERR_INVALID_ARG, "bias dtype %d", bias_dtype);
     if (bias_sb < 0 || bias_sh < 0) return fail(QFA_ERR_INVALID_ARG, "negative bias stride");
     if (index) return fail(QFA_ERR_INVALID_ARG, "bias and block-sparse mask are mutually exclusive");

@@ -191,7 +191,7 @@ __device__ __forceinline__ unsigned lds_addr(const T* p) {
 }
 
 // Global -> LDS copy of one lane-linear block: lane l's SIZE bytes (16, 4,
-// or 2 zero-extended to 4) land at lds + l*max(SIZE,4). Written as inline
+// or 2 or 1 zero-extended to 4) land at lds + l*max(SIZE,4). Written as inline
 // assembly so that the compiler neither waits on these copies before
 // unrelated LDS reads nor counts them: every wait for them is explicit
 // (wait_vmcnt / stage_barrier), and the loop issues no other vector-memory
@@ -209,8 +209,11 @@ __device__ __forceinline__ void lds_copy(unsigned lds, int voff, v4u desc) {
   else if constexpr (SIZE == 4)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
-  else
+  else if constexpr (SIZE == 2)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
                  :: "s"(lds), "v"(voff), "s"(desc) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -427,6 +430,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const float* ksbase = a.ks + (int64_t)bh * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
+  // unbiased instances take a [1,1,1,K] keep mask (bool bytes) through the
+  // key terms: a masked key is excluded like a segment edge, at no per-score cost
+  const int keep_mask = (!HAS_BIAS && !SPARSE && !DUMP && a.bias != nullptr) ? 1 : 0;
 
   // per-lane source offsets of this wave's copy instructions (tile-relative)
   int k_src[KI_W], v_src[VI_W];
@@ -463,8 +469,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     for (int i = 0; i < VI_W; ++i) lds_copy<16>(lds_addr(&vbuf[stage][(wave + i * NW) * 1024]), v_src[i], d);
   };
   // raw key terms of a tile: wave 0 copies the key scales of keys
-  // key0 + lane, wave 1 the bias values (range [lo, hi): keys outside it
-  // read zero and are excluded when the terms are derived)
+  // key0 + lane, wave 1 the bias values, or (unbiased kernel with a keep
+  // mask) the mask bytes (range [lo, hi): keys outside it read zero and are
+  // excluded when the terms are derived)
   auto copy_terms = [&](int stage, int tile, int lo, int hi, int valid) __attribute__((always_inline)) {
     if constexpr (DUMP) return;
     const int nk = valid ? hi - lo : 0;
@@ -475,6 +482,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       const v4u d = buf_desc32((const unsigned char*)a.bias + (bias_off + lo) * bias_esz, nk * bias_esz);
       if (bias_esz == 4) lds_copy<4>(lds_addr(&kt[stage].raw[1][0]), rel * 4, d);
       else lds_copy<2>(lds_addr(&kt[stage].raw[1][0]), rel * 2, d);
+    } else if (!HAS_BIAS && keep_mask && wave == 1) {
+      lds_copy<1>(lds_addr(&kt[stage].raw[1][0]), rel, buf_desc32((const unsigned char*)a.bias + bias_off + lo, nk));
     }
   };
   // derive the terms of a tile from its copied raw values (the calling
@@ -488,8 +497,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     if (wave == 0) {
       const float ks = in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f;
       kt[stage].sc[0][lane] = ks;
-      // an excluded key dequantizes to fma(x, 0, -inf) = -inf
-      const bool in_a = in && (!SPARSE || (flags & 2));
+      // an excluded key dequantizes to fma(x, 0, -inf) = -inf; a keep mask
+      // (copied by wave 1) excludes its zero entries the same way
+      const bool keep = HAS_BIAS || !keep_mask || kt[stage].raw[1][lane] != 0u;
+      const bool in_a = in && keep && (!SPARSE || (flags & 2));
       kt[stage].sc[1][lane] = in_a ? -kMagic * ks : -INFINITY;
       if (SPARSE) kt[stage].sc[3][lane] = in && (flags & 4) ? -kMagic * ks : -INFINITY;
     } else if (HAS_BIAS && wave == 1) {
@@ -539,6 +550,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_v(0, t0, v0);
     copy_k(1, t1, v1);
     wait_vmcnt<0>();
+    // the keep-mask bytes wave 0 folds in were copied by wave 1
+    if (keep_mask) stage_barrier<0>();
     derive_terms(0, t0, l0, h0, v0);
     stage_barrier<0>();
     qk_block(0, 0);
@@ -721,7 +734,7 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   if (sparse) {
     if (a.lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, true, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
-  } else if (a.bias) {
+  } else if (a.bias && a.bias_dtype != BOOL) {
     if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);
   } else {

@@ -7,7 +7,7 @@
 
 namespace qfa {
 
-enum DType : int { BF16 = 1, FP16 = 2, FP32 = 3 };
+enum DType : int { BF16 = 1, FP16 = 2, FP32 = 3, BOOL = 4 };
 
 // K mean: partial sums per (bh, chunk) in double-double, then one finalize.
 constexpr int kMeanChunkRows = 256;
@@ -56,7 +56,7 @@ struct AttnArgs {
   int v_dtype;
   int64_t v_sb, v_sh, v_ss;
   float sm_scale;
-  const void* bias;     // nullable
+  const void* bias;     // nullable; bias_dtype BOOL: a keep mask (nonzero bytes attend)
   int bias_dtype;
   int64_t bias_sb, bias_sh;
   const int32_t* index; // nullable (dense)

@@ -227,6 +227,31 @@ def test_attn_edge_cases():
     assert out.shape[2] == 0
 
 
+def test_keep_mask():
+    """A bool [1,1,1,K] keep mask (True attends) equals the additive bias 0 / -inf: the banded
+    weights thresholded at 1e-3, a random mask over key segments, and an all-false mask (every
+    row O = 0, LSE = -inf)."""
+    w = W.WORKLOADS["band"]
+    Sk = 1680
+    q, k, v = W.make_qkv(w, H=2, Sq=256, Sk=Sk)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    tv = up(v)
+    weights = np.exp(W.band_bias(Sk, core=(336, 1008), skirt=336))
+    rs = np.random.default_rng(11)
+    segs = [(0, 700), (900, 780)]
+    cases = [("band keep w > 1e-3", weights > 1e-3, None), ("random over segments", rs.random(Sk) < 0.6, segs),
+             ("all masked", np.zeros(Sk, bool), None)]
+    for what, keep, seg in cases:
+        keep4 = keep.reshape(1, 1, 1, Sk)
+        add = np.where(keep4, 0.0, -np.inf).astype(np.float32)
+        o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=add, segments=seg)
+        o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=torch.from_numpy(keep4).to(tv.device), segments=seg,
+                            return_lse=True)
+        check_o(o, o_ref, what=what)
+        check_lse(l, l_ref, what=what)
+
+
 def test_attn_deterministic():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
