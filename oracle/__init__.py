@@ -64,7 +64,7 @@ def _declare(L):
     L.oracle_scores_i32.argtypes = [_P, _P, _I64, _I64, _I64, _P]
     L.oracle_attn.argtypes = ([_I64] * 5 + [_P] * 6 + [_P, ctypes.c_int, ctypes.c_float]
                               + [_P, ctypes.c_int, _I64, _I64, _I64, _I64]
-                              + [_P, _P, _P, ctypes.c_int, _P, _P, _P, _I64, _P, _P])
+                              + [_P, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I64, _P, _P])
     L.oracle_lse_merge.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P]
     L.oracle_blockmask_to_index.argtypes = [_P, _I64, _I64, _P, _P]
     for f in (L.oracle_kmean, L.oracle_quantize_rows, L.oracle_qmu, L.oracle_scores_i32,
@@ -161,12 +161,13 @@ def _bias_args(bias, B, H, Sq, Sk):
 def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | None = None,
          k: np.ndarray | None = None, bias: np.ndarray | None = None, mask: np.ndarray | None = None,
          vbs: np.ndarray | None = None, v_scale: np.ndarray | None = None, segments=None,
-         rows: np.ndarray | None = None, use_qmu: bool = True):
+         rows: np.ndarray | None = None, use_qmu: bool = True, causal: bool = False):
     """Attention in fp64 for all rows (or the flat [B,H,Sq] row indices in ``rows``).
 
     Quantized mode: ``qk`` is the dict from :func:`quantize_qk` (or the same
     fields from any source). No-quant mode: ``qk`` is None and raw ``q``/``k``
-    (any float arrays) are used in fp64. Returns (O [nrows, D] f64, LSE [nrows] f64).
+    (any float arrays) are used in fp64. ``causal`` (self-attention, Sq == Sk)
+    excludes every key j > i from row i. Returns (O [nrows, D] f64, LSE [nrows] f64).
     """
     v = _c(v)
     B, H, Sk, D = v.shape
@@ -181,6 +182,8 @@ def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | Non
         Sq = qf.shape[2]
         q8 = qs = k8 = ks = None
         qm = None
+    if causal and Sq != Sk:
+        raise ValueError("causal attention is defined here for self-attention (Sq == Sk)")
     base, b4, bdt, bsb, bsh, bsq, bsk = _bias_args(bias, B, H, Sq, Sk)
     mask = _c(mask, np.uint8)
     vbs = _c(vbs, np.int32)
@@ -201,7 +204,7 @@ def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | Non
     bptr = None if b4 is None else ctypes.c_void_p(b4.__array_interface__["data"][0])
     lib().oracle_attn(B, H, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(qf), _ptr(kf),
                       _ptr(v), dtype_code(v), float(sm_scale), bptr, bdt, bsb, bsh, bsq, bsk,
-                      _ptr(mask), _ptr(vbs), _ptr(v_scale), nseg, _ptr(seg), _ptr(qm),
+                      _ptr(mask), _ptr(vbs), _ptr(v_scale), nseg, _ptr(seg), _ptr(qm), int(bool(causal)),
                       _ptr(rows), nrows, _ptr(o), _ptr(lse))
     del base
     return o, lse

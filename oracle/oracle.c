@@ -204,8 +204,8 @@ void oracle_scores_i32(const int8_t* q8, const int8_t* k8, int64_t Sq, int64_t S
  * fp64 operands (q8 == NULL, qf/kf given):
  *     s_ij = sm_scale * sum_c Q_ic K_jc + bias_ij.
  * A key is excluded (s = -inf) when it lies outside every segment, when the
- * block mask drops its tile or it is a pad key of its tile, or when its
- * bias is -inf.
+ * block mask drops its tile or it is a pad key of its tile, when its
+ * bias is -inf, or (causal, self-attention: Sq = Sk) when j > i.
  *
  * Layouts (all contiguous except the bias, which takes element strides so
  * that a [1,1,1,K] stride-0 broadcast and its [B,H,Q,K] expansion are both
@@ -227,7 +227,7 @@ void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  const void* v, int v_dtype, float sm_scale,
                  const void* bias, int bias_dtype, int64_t bsb, int64_t bsh, int64_t bsq, int64_t bsk,
                  const uint8_t* mask, const int32_t* vbs,
-                 const float* v_scale, int nseg, const int64_t* seg, const double* qmu,
+                 const float* v_scale, int nseg, const int64_t* seg, const double* qmu, int causal,
                  const int64_t* rows, int64_t nrows, double* o, double* lse) {
     int64_t Tq = Sq / 64, Tk = Sk / 64;
     if (rows == NULL) nrows = B * H * Sq;
@@ -245,6 +245,7 @@ void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                 if (!mask[(bh * Tq + i / 64) * Tk + j / 64]) keep = 0;
                 if (is_pad_row(vbs, j)) keep = 0;
             }
+            if (causal && j > i) keep = 0;
             double sij = -INFINITY;
             if (keep) {
                 double dot;

@@ -15,16 +15,18 @@ import torch
 import workloads as W
 
 
-def _sdpa64(q, k, v, scale, mask=None):
+def _sdpa64(q, k, v, scale, mask=None, is_causal=False):
     """fp64 CPU SDPA and its log-sum-exp, the library reference for no-quant attention."""
     qt = torch.tensor(W.to_f32(q), dtype=torch.float64)
     kt = torch.tensor(W.to_f32(k), dtype=torch.float64)
     vt = torch.tensor(W.to_f32(v), dtype=torch.float64)
     m = None if mask is None else torch.tensor(mask, dtype=torch.float64)
-    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale, is_causal=is_causal)
     s = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
     if m is not None:
         s = s + m
+    if is_causal:
+        s = s.masked_fill(torch.ones(s.shape[-2:], dtype=torch.bool).triu(1), -math.inf)
     lse = torch.logsumexp(s, dim=-1)
     return o.numpy(), lse.numpy()
 
@@ -40,6 +42,30 @@ def test_noquant_matches_sdpa(oracle_lib):
     ro, rl = _sdpa64(q, k, v, w.sm_scale)
     assert np.max(np.abs(o - ro.reshape(-1, 128))) < 1e-12
     assert np.max(np.abs(lse - rl.reshape(-1))) < 1e-12
+
+
+def test_noquant_causal_matches_sdpa(oracle_lib):
+    # self-attention with the key range ending at each row (torch's is_causal)
+    w, (q, k, v) = _small(Sq=160, Sk=160)
+    o, lse = oracle_lib.attn(None, v, w.sm_scale, q=W.to_f32(q), k=W.to_f32(k), causal=True)
+    ro, rl = _sdpa64(q, k, v, w.sm_scale, is_causal=True)
+    assert np.max(np.abs(o - ro.reshape(-1, 128))) < 1e-12
+    assert np.max(np.abs(lse - rl.reshape(-1))) < 1e-12
+
+
+def test_causal_equals_triangular_bias(oracle_lib):
+    # quantized mode: the causal exclusion and a materialised 0 / -inf upper-triangular bias are
+    # two code paths to one definition; row 0 sees key 0 alone, so its output is V[0] exactly
+    w, (q, k, v) = _small(Sq=200, Sk=200)
+    qk = oracle_lib.quantize_qk(q, k)
+    tri = np.where(np.triu(np.ones((200, 200), bool), 1), -np.inf, 0.0).astype(np.float32).reshape(1, 1, 200, 200)
+    o_c, l_c = oracle_lib.attn(qk, v, w.sm_scale, causal=True)
+    o_b, l_b = oracle_lib.attn(qk, v, w.sm_scale, bias=tri)
+    assert np.array_equal(o_c, o_b) and np.array_equal(l_c, l_b)
+    v0 = W.to_f32(v)[0, :, 0, :].astype(np.float64)     # [H, D]
+    assert np.array_equal(o_c.reshape(1, 2, 200, 128)[0, :, 0, :], v0)
+    with pytest.raises(ValueError):
+        oracle_lib.attn(qk, v[:, :, :100], w.sm_scale, causal=True)
 
 
 def test_noquant_full_bias_matches_sdpa(oracle_lib):
