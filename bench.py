@@ -272,7 +272,7 @@ def main() -> int:
 
 
 COPY_BYTES = 256 << 20
-UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false, false>"
+UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false, false, false>"
 
 
 def _counter_per_dispatch(path: str, counter: str):
@@ -363,7 +363,8 @@ def _time_ms(fn, iters: int, warmup: int = 3) -> float:
 
 def other_configs(dev) -> int:
     """One JSON line per configuration besides the step's banded workload: quantize and attention
-    times, effective TFLOPS (4*B*H*Sq*Sk_eff*D; block-sparse counts the selected 64x64 tile pairs)
+    times, effective TFLOPS (4*B*H*Sq*Sk_eff*D; block-sparse counts the selected 64x64 tile pairs,
+    causal the S(S+1)/2 attended pairs)
     and the fraction of the blended int8/bf16 MFMA peak; quantize / map-to-index bandwidth against
     HBM's 8 TB/s. Last, a bf16 and an int8 GEMM through torch as an on-box matrix-core reference."""
     import numpy as np
@@ -393,7 +394,9 @@ def other_configs(dev) -> int:
         t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
         t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out), 20)
         t_l = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out, lse=lse), 20)
+        t_c = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, causal=True, out=out), 20)
         fl = 4.0 * w.B * w.H * w.Sq * w.Sk * w.D
+        fl_c = 4.0 * w.B * w.H * w.D * (w.Sq * (w.Sq + 1) / 2)   # attended (row, key) pairs j <= i
         qb = qbytes(w.B, w.H, w.Sq, w.Sk, w.D, 2)
         print(json.dumps({
             "config": name, "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} {w.dtype}",
@@ -401,7 +404,9 @@ def other_configs(dev) -> int:
             "quantize_frac_hbm": round(qb / (t_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
             "attn_ms": round(t_a, 4), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
             "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
-            "attn_lse_ms": round(t_l, 4), "lse_over_plain": round(t_l / t_a, 3), "device": info}), flush=True)
+            "attn_lse_ms": round(t_l, 4), "lse_over_plain": round(t_l / t_a, 3),
+            "causal_ms": round(t_c, 4), "causal_tflops": round(fl_c / (t_c * 1e-3) / 1e12, 1),
+            "causal_frac_blend": round(fl_c / (t_c * 1e-3) / 1e12 / PEAK_BLEND, 4), "device": info}), flush=True)
         del q, k, v, qk, out, lse, ws
         torch.cuda.empty_cache()
 

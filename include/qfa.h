@@ -168,6 +168,13 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * v_scale:  nullable fp32 [H,D] per-(head,channel) factor applied to O.
  * nseg, seg: host array of nseg (<= 4) (start, length) pairs of key ranges,
  *           ascending and disjoint; nseg = 0 means the whole [0, Sk).
+ * causal:   nonzero: causal self-attention, row i attends keys j <= i only
+ *           (the causal mode that ROCm/FlyDSL PR #886 tests and times,
+ *           "Test Plan"; read as self-attention, key j <= row i). Needs Sq == Sk
+ *           (else QFA_ERR_INVALID_ARG); combines with a bias or keep mask,
+ *           v_scale and the LSE, not with segments or a block-sparse mask
+ *           (QFA_ERR_UNSUPPORTED). The walk of each 128-row block stops at
+ *           its last row's key, so about half the key tiles are read.
  * out:      [B,H,Sq,D] of out_dtype (QFA_BF16, QFA_FP16 or QFA_FP32), strides
  *           (o_sb, o_sh, o_ss); base and row strides 16-byte aligned.
  * lse:      nullable fp32 [B,H,Sq] contiguous output; non-NULL requests it.
@@ -180,7 +187,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  float sm_scale,
                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
                  const int32_t* index, const int32_t* count, const int32_t* vbs,
-                 const float* v_scale, int nseg, const int64_t* seg,
+                 const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                  float* lse, void* stream);
 

@@ -131,8 +131,9 @@ def qk_scores_i32(q8: torch.Tensor, k8: torch.Tensor) -> torch.Tensor:
 
 def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,
              index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
-             v_scale: torch.Tensor | None = None, segments=None, out: torch.Tensor | None = None,
-             out_dtype: torch.dtype | None = None, return_lse: bool = False, lse: torch.Tensor | None = None):
+             v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
+             out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None, return_lse: bool = False,
+             lse: torch.Tensor | None = None):
     """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
 
     bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
@@ -141,6 +142,7 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
         the key terms at no per-score cost.
     index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
     segments: up to 4 ascending disjoint (start, length) key ranges.
+    causal: self-attention (Sq == Sk) where row i attends keys j <= i only.
     return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
     """
     _no_grad(v, bias)
@@ -186,7 +188,7 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
         B, H, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
         _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
         bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
-        _ptr(out), do, *ost, _ptr(lse), _stream(dev)))
+        int(bool(causal)), _ptr(out), do, *ost, _ptr(lse), _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 
@@ -212,7 +214,7 @@ def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: 
 
 def int8_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
                    attn_mask: torch.Tensor | None = None, *, return_lse: bool = False, center_k: bool = True,
-                   segments=None):
+                   segments=None, is_causal: bool = False):
     """Quantize Q/K once and attend (the comfy-kitchen-style entry point).
 
     attn_mask: a per-key additive float bias [B|1,H|1,1|Q,K] (stride-0 over Q).
@@ -220,7 +222,7 @@ def int8_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: flo
     qk = quantize_qk(q, k, center_k=center_k)
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    return attn_fwd(qk, v, scale, bias=attn_mask, segments=segments, return_lse=return_lse)
+    return attn_fwd(qk, v, scale, bias=attn_mask, segments=segments, causal=is_causal, return_lse=return_lse)
 
 
 def sm_scale_default(D: int) -> float:

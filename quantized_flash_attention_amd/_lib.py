@@ -53,7 +53,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_blockmask_to_index.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.qfa_blockmask_to_index.restype = _I
     L.qfa_attn_fwd.argtypes = ([_I64] * 5 + [_P] * 5 + [_P, _I, _I64, _I64, _I64] + [ctypes.c_float]
-                               + [_P, _I, _I64, _I64] + [_P] * 3 + [_P, _I, _P]
+                               + [_P, _I, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
                                + [_P, _I, _I64, _I64, _I64] + [_P, _P])
     L.qfa_attn_fwd.restype = _I
     L.qfa_lse_merge.argtypes = ([_I64] * 4 + [_P, _I, _I64, _I64, _I64, _P] * 2

@@ -159,7 +159,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  float sm_scale,
                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
                  const int32_t* index, const int32_t* count, const int32_t* vbs,
-                 const float* v_scale, int nseg, const int64_t* seg,
+                 const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                  float* lse, void* stream) {
   int st;
@@ -194,6 +194,15 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
     if (Sq != Sk || Sk % 64) return fail(QFA_ERR_INVALID_ARG, "block-sparse needs Sq == Sk, a multiple of 64");
     if (nseg != 0) return fail(QFA_ERR_INVALID_ARG, "segments are not combinable with a block-sparse mask");
   }
+  if (causal) {
+    if (Sq != Sk) return fail(QFA_ERR_INVALID_ARG, "causal attention needs Sq == Sk (got %lld, %lld)", (long long)Sq, (long long)Sk);
+    if (index) return fail(QFA_ERR_UNSUPPORTED, "causal attention with a block-sparse mask");
+    if (nseg != 0) return fail(QFA_ERR_UNSUPPORTED, "causal attention with key segments");
+  }
+  // one 128-row block per (query tile, head), heads padded to 8 for causal calls;
+  // 256 threads per block keep the launch within 2^32 threads
+  if ((Sq + 127) / 128 * ((B * H + 7) / 8 * 8) > (1ll << 24))
+    return fail(QFA_ERR_UNSUPPORTED, "more than 2^24 blocks of 128 query rows");
   if (nseg < 0 || nseg > QFA_MAX_SEGMENTS) return fail(QFA_ERR_INVALID_ARG, "nseg %d (0..4)", nseg);
   if (nseg > 0 && !seg) return fail(QFA_ERR_INVALID_ARG, "seg is NULL with nseg > 0");
   int64_t prev_end = 0;
@@ -212,6 +221,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
     nseg = 1;
   }
   a.nseg = nseg;
+  a.causal = causal ? 1 : 0;
   a.B = (int)B; a.H = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
   a.q8 = q8; a.qs = qs; a.qmu = qmu; a.k8 = k8; a.ks = ks;
   a.v = v; a.v_dtype = v_dtype; a.v_sb = v_sb; a.v_sh = v_sh; a.v_ss = v_ss;

@@ -25,15 +25,18 @@
 //            channel per lane), and O^T leaves each lane holding 16 channels
 //            of its own query row per 32-channel block, so the online-softmax
 //            rescale is a per-lane scalar.
-//   keys   = 64 per tile. K8/V tiles are staged global -> VGPR (prefetch of
-//            the next tile while the current one is computed) -> LDS.
+//   keys   = 64 per tile. K8/V tiles and the raw key terms go global -> LDS
+//            by buffer loads that write LDS directly, into a 3-stage ring
+//            (copies run two tiles ahead of the MFMAs).
 //   grid   = 1-D, remapped so that the blocks one XCD runs cover whole heads
 //            (consecutive block ids are dealt round-robin to the 8 XCDs);
-//            blocks sharing K/V then share that XCD's L2.
+//            blocks sharing K/V then share that XCD's L2. Causal calls order
+//            the blocks by walk length instead (causal_order).
 #include "qfa_internal.h"
 
 #include <float.h>
 
+#include <atomic>
 #include <type_traits>
 
 namespace qfa {
@@ -76,6 +79,21 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   const int per = total / 8, rem = total % 8;
   const int xcd = L % 8, slot = L / 8;
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Causal launches: dispatch index k -> work index L. Work is numbered by
+// query-tile rank (longest walk first), then head, over a head count padded
+// to a multiple of 8, so that a head's blocks share one XCD (k mod 8) and
+// padding blocks exit at once. Blocks k and k + ncu start on the same CU, so
+// the second round of ncu blocks runs in reverse (in groups of 8, keeping
+// k mod 8): each CU then pairs a long walk with a short one. Any order is
+// correct; this one balances the first two rounds, and later blocks take
+// freed slots longest first.
+__device__ __forceinline__ int causal_order(int k, int total, int ncu) {
+  if (ncu % 8 != 0 || k < ncu || k >= 2 * ncu) return k;
+  const int m = min(total, 2 * ncu) - ncu;   // blocks of the second round
+  const int j = k - ncu;
+  return m % 8 == 0 ? ncu + (m / 8 - 1 - j / 8) * 8 + j % 8 : ncu + (m - 1 - j);
 }
 
 __device__ __forceinline__ float load_bias(const void* p, int dtype, int64_t idx) {
@@ -323,7 +341,13 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 // through the same copies, LDS layout, MFMA and seeded accumulators, and
 // skip V, the key terms and the softmax. They exist to check those scores
 // bit for bit.
-template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false>
+//
+// CAUSAL instances (dense, one segment [0, Sk), Sq == Sk) stop each block's
+// walk at the tile holding its last row's key; the (at most two) tiles that
+// cross the block's diagonal run in a loop of their own that sets the scores
+// of keys past the row to -inf, so the main loop is the plain one. Blocks
+// run heaviest first.
+template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false, bool CAUSAL = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
   constexpr int KC = D / 32;                     // int8 MFMA k-steps / 32-channel blocks
@@ -340,8 +364,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NSTG][V_BYTES];
   __shared__ __attribute__((aligned(16))) KeyTerms kt[NSTG];
 
-  const int bid = xcd_remap((int)blockIdx.x, total_blocks);
-  const int bh = bid / qtiles, qt = bid % qtiles;
+  int bh, qt;
+  if constexpr (CAUSAL) {
+    const int L = causal_order((int)blockIdx.x, total_blocks, a.ncu);
+    const int bh8 = total_blocks / qtiles;
+    bh = L % bh8;
+    qt = qtiles - 1 - L / bh8;
+    if (bh >= a.B * a.H) return;   // head padding: the whole block leaves before any barrier
+  } else {
+    const int bid = xcd_remap((int)blockIdx.x, total_blocks);
+    bh = bid / qtiles;
+    qt = bid % qtiles;
+  }
   const int b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -371,6 +405,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     n_tiles = INT32_MAX;   // the length of the union, known once the walk reaches its end
   } else {
     n_tiles = a.seg_ntiles;
+    if constexpr (CAUSAL) n_tiles = min(n_tiles, (min(a.Sk, qt * BM + BM) + BN - 1) / BN);
   }
   const __attribute__((address_space(4))) int32_t* vbs = (const __attribute__((address_space(4))) int32_t*)a.vbs;
   // The key tiles of this block in loop order, one per call: the tile, the
@@ -565,7 +600,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 
   // One tile. Excluded keys (segment edges, pad keys of block-sparse tiles)
   // carry -inf in their key terms, so every tile runs the same code.
-  auto tile_body = [&](int iter, int st0, int st1, int st2) __attribute__((always_inline)) {
+  // `diag` (a literal at each call): the tile may hold keys past some row
+  auto tile_body = [&](int iter, int st0, int st1, int st2, bool diag) __attribute__((always_inline)) {
     // st0 = iter % 3, st1 = (iter + 1) % 3, st2 = (iter + 2) % 3
     const KeyTerms& tc = kt[st0];
     int t3, l3, h3, v3;
@@ -627,6 +663,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       if (blk == 0) copy_k(iter % 3, t3, v3);   // K(iter+3) over K(iter)
     }
     copy_v(st2, t2, v2);                        // V(iter+2) over V(iter-1)
+    if (CAUSAL && diag) {
+      // the walk is the single segment [0, Sk), so tile `iter` holds keys
+      // iter*BN + [0, BN); only waves whose first row lies before the tile's
+      // last key see a key past their row
+      if (qt * BM + wave * 32 < iter * BN + BN - 1) {
+        const int lim = q - iter * BN;   // last attended key of this row, tile-relative
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (32 * blk + 8 * g + 4 * hl + r > lim) t[blk][4 * g + r] = -INFINITY;
+      }
+    }
     // crow > 0, so max(u)*crow = max(u*crow) (also for -inf)
     const float mx = (HAS_BIAS) ? xmax32(max32(t)) : xmax32(max32(t)) * crow;
 
@@ -710,13 +761,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     v2 = v3;
   };
 
+  // causal: tiles [0, n_plain) hold no key past the block's first row and
+  // run the plain body; the (at most two) tiles across the diagonal run a
+  // copy with the mask, so the main loop carries none of its code. Other
+  // instances test n_tiles itself on every pass: a block-sparse walk sets
+  // it (from INT32_MAX) only when its lists run out.
+  const int n_plain = CAUSAL ? min(n_tiles, (qt * BM + 1) / BN) : 0;
   int st0 = 0, st1 = 1, st2 = 2;
-  for (int iter = 0; iter < n_tiles; ++iter) {
-    tile_body(iter, st0, st1, st2);
+  int iter = 0;
+  for (; iter < (CAUSAL ? n_plain : n_tiles); ++iter) {
+    tile_body(iter, st0, st1, st2, false);
     const int tmp = st0;
     st0 = st1;
     st1 = st2;
     st2 = tmp;
+  }
+  if constexpr (CAUSAL) {
+    for (; iter < n_tiles; ++iter) {
+      tile_body(iter, st0, st1, st2, true);
+      const int tmp = st0;
+      st0 = st1;
+      st1 = st2;
+      st2 = tmp;
+    }
   }
   // drain this wave's remaining copies (they target stages nobody reads)
   wait_vmcnt<0>();
@@ -734,6 +801,17 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   if (sparse) {
     if (a.lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, true, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
+  } else if (a.causal) {
+    // a keep mask (bool bias) runs in the unbiased instance; the grid pads
+    // B*H to a multiple of 8 (see causal_order)
+    const int total8 = qtiles * ((a.B * a.H + 7) / 8 * 8);
+    if (a.bias && a.bias_dtype != BOOL) {
+      if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      else attn_fwd_kernel<D, VT, 4, false, true, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+    } else {
+      if (a.lse) attn_fwd_kernel<D, VT, 4, false, false, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      else attn_fwd_kernel<D, VT, 4, false, false, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+    }
   } else if (a.bias && a.bias_dtype != BOOL) {
     if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);
@@ -776,6 +854,20 @@ hipError_t launch_qk_scores(const AttnArgs& args, hipStream_t s) {
 hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
   AttnArgs a = args;
   derive_segments(a);
+  if (a.causal) {
+    // compute units of the current device, queried once per device
+    static std::atomic<int> ncu_of[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int ncu = dev >= 0 && dev < 64 ? ncu_of[dev].load(std::memory_order_relaxed) : 0;
+    if (ncu == 0) {
+      e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      if (dev >= 0 && dev < 64) ncu_of[dev].store(ncu, std::memory_order_relaxed);
+    }
+    a.ncu = ncu;
+  }
   if (a.D == 128) return a.v_dtype == BF16 ? launch_d_vt<128, BF16>(a, s) : launch_d_vt<128, FP16>(a, s);
   return a.v_dtype == BF16 ? launch_d_vt<64, BF16>(a, s) : launch_d_vt<64, FP16>(a, s);
 }

@@ -65,6 +65,8 @@ struct AttnArgs {
   const float* v_scale; // nullable [H, D]
   int nseg;
   int seg_lo[4], seg_hi[4];
+  int causal;           // self-attention with key j > row i excluded (Sq == Sk, one segment [0, Sk))
+  int ncu;              // compute units of the device (block order of causal calls)
   // derived by the launcher from the segments: first key tile of segment g,
   // number of tiles before segment g (INT32_MAX for absent segments), and
   // the total number of key tiles of the call

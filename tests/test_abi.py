@@ -63,12 +63,12 @@ def test_quantize_rejects_bad_arguments():
 
 def _attn(**kw):
     a = dict(B=1, H=2, Sq=128, Sk=128, D=128, qk=[FAKE] * 5, v=FAKE, vdt=1, v_s=(32768, 16384, 128), scale=0.088,
-             bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None,
+             bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None, causal=0,
              out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
     a.update(kw)
     return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
                                    ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a["index"],
-                                   a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["out"], a["odt"],
+                                   a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["causal"], a["out"], a["odt"],
                                    *a["o_s"], a["lse"], None)
 
 
@@ -97,6 +97,11 @@ def test_attn_rejects_bad_arguments():
     assert _attn(nseg=2, seg=_segs((60, 10), (0, 10))) == _lib.QFA_ERR_INVALID_ARG   # descending
     assert _attn(out=ctypes.c_void_p(0x10004)) == _lib.QFA_ERR_INVALID_ARG
     assert _attn(vsc=ctypes.c_void_p(0x10004)) == _lib.QFA_ERR_INVALID_ARG
+    # causal: self-attention only; not with segments or a block-sparse mask
+    assert _attn(causal=1, Sk=256, v_s=(65536, 32768, 128)) == _lib.QFA_ERR_INVALID_ARG
+    assert b"Sq == Sk" in _lib.lib().qfa_last_error()
+    assert _attn(causal=1, nseg=1, seg=_segs((0, 128))) == _lib.QFA_ERR_UNSUPPORTED
+    assert _attn(causal=1, index=FAKE, count=FAKE) == _lib.QFA_ERR_UNSUPPORTED
 
 
 def test_merge_rejects_bad_arguments():

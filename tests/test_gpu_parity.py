@@ -252,6 +252,63 @@ def test_keep_mask():
         check_lse(l, l_ref, what=what)
 
 
+CAUSAL_CASES = {
+    # (workload, B, H, S, bias): S spans one key, partial first tiles, whole and ragged
+    # 128-row blocks (the two diagonal tiles of a block) and several blocks
+    "S1": ("dense4k", 1, 1, 1, None),
+    "S64": ("dense4k", 1, 2, 64, None),
+    "S129": ("dense4k", 1, 2, 129, None),
+    "ragged_333": ("dense4k", 1, 2, 333, None),
+    "d64_fp16_517": ("d64", 2, 2, 517, None),
+    "bias_fp32_700": ("band", 1, 2, 700, "fp32"),
+    "keep_mask_640": ("band", 1, 2, 640, "keep"),
+}
+
+
+@pytest.mark.parametrize("case", list(CAUSAL_CASES))
+@pytest.mark.parametrize("lse", [True, False])
+def test_causal_parity(case, lse):
+    """Causal self-attention (key j attended by row i iff j <= i) against the oracle, with and
+    without the LSE (different kernel instances), alone and with a bias or a keep mask."""
+    wn, B, H, S, bias_kind = CAUSAL_CASES[case]
+    w = W.WORKLOADS[wn]
+    q, k, v = W.make_qkv(w, B=B, H=H, Sq=S, Sk=S)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    bias_ref = bias_gpu = None
+    if bias_kind == "fp32":
+        bias_ref = W.bias_tensor(W.band_bias(S, core=(S // 5, S - 2 * (S // 5)), skirt=S // 5), "fp32")
+        bias_gpu = up(bias_ref)
+    elif bias_kind == "keep":
+        keep = (np.random.default_rng(5).random(S) < 0.7).reshape(1, 1, 1, S)
+        keep[..., 0] = False   # row 0 then attends nothing: O = 0, LSE = -inf
+        bias_ref = np.where(keep, 0.0, -np.inf).astype(np.float32)
+        bias_gpu = torch.from_numpy(keep).to(DEV)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias_ref, causal=True)
+    res = qfa.attn_fwd(g, up(v), w.sm_scale, bias=bias_gpu, causal=True, return_lse=lse)
+    o = res[0] if lse else res
+    check_o(o, o_ref, what=f"causal {case}")
+    if lse:
+        check_lse(res[1], l_ref, what=f"causal {case}")
+    if bias_kind == "keep":
+        assert torch.all(o[:, :, 0] == 0)
+
+
+def test_causal_full_size_sampled():
+    """B1 H16 S4096 D128 causal: sampled rows plus the rows around block and tile edges."""
+    w = W.WORKLOADS["dense4k"]
+    q, k, v = W.make_qkv(w)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=24)
+    edges = np.array([0, 1, 63, 64, 127, 128, 129, 2047, 2048, 4031, 4032, 4095])
+    rows = np.unique(np.r_[rows, edges, 5 * w.Sq + edges])
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, causal=True, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows, causal=True)
+    check_o(o, o_ref, rows, "causal full")
+    check_lse(l, l_ref, rows, "causal full")
+
+
 def test_attn_deterministic():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
