@@ -60,9 +60,9 @@ _I64 = ctypes.c_int64
 def _declare(L):
     L.oracle_kmean.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P]
     L.oracle_quantize_rows.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P]
-    L.oracle_qmu.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P]
+    L.oracle_qmu.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.oracle_scores_i32.argtypes = [_P, _P, _I64, _I64, _I64, _P]
-    L.oracle_attn.argtypes = ([_I64] * 5 + [_P] * 6 + [_P, ctypes.c_int, ctypes.c_float]
+    L.oracle_attn.argtypes = ([_I64] * 6 + [_P] * 6 + [_P, ctypes.c_int, ctypes.c_float]
                               + [_P, ctypes.c_int, _I64, _I64, _I64, _I64]
                               + [_P, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I64, _P, _P])
     L.oracle_lse_merge.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P]
@@ -114,19 +114,28 @@ def quantize_rows(x: np.ndarray, mean: np.ndarray | None = None, vbs: np.ndarray
     return q, s
 
 
+def _kv_heads(H: int, Hkv: int) -> int:
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{H} query heads cannot share {Hkv} K/V heads")
+    return Hkv
+
+
 def qmu(q: np.ndarray, mean: np.ndarray, vbs: np.ndarray | None = None) -> np.ndarray:
-    """Centring term sum_c Q_ic * mu_c in fp64: -> [B,H,S]."""
+    """Centring term sum_c Q_ic * mu_c in fp64: -> [B,H,S]. ``mean`` is [B,Hkv,D]; query
+    head h uses the mean of K/V head h // (H // Hkv)."""
     q = _c(q)
     B, H, S, D = q.shape
     mean = _c(mean, np.float32)
+    Hkv = _kv_heads(H, mean.shape[1])
     vbs = _c(vbs, np.int32)
     out = np.empty((B, H, S), np.float64)
-    lib().oracle_qmu(_ptr(q), dtype_code(q), B, H, S, D, _ptr(mean), _ptr(vbs), _ptr(out))
+    lib().oracle_qmu(_ptr(q), dtype_code(q), B, H, Hkv, S, D, _ptr(mean), _ptr(vbs), _ptr(out))
     return out
 
 
 def quantize_qk(q: np.ndarray, k: np.ndarray, vbs: np.ndarray | None = None, center_k: bool = True) -> dict:
-    """The whole quantize step: K mean, Q and centred-K int8 + scales, centring term."""
+    """The whole quantize step: K mean, Q and centred-K int8 + scales, centring term.
+    K may hold fewer heads than Q (grouped-query attention, reading R8 of oracle.c)."""
     mu = kmean(k, vbs) if center_k else None
     q8, qs = quantize_rows(q, None, vbs)
     k8, ks = quantize_rows(k, mu, vbs)
@@ -167,10 +176,12 @@ def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | Non
     Quantized mode: ``qk`` is the dict from :func:`quantize_qk` (or the same
     fields from any source). No-quant mode: ``qk`` is None and raw ``q``/``k``
     (any float arrays) are used in fp64. ``causal`` (self-attention, Sq == Sk)
-    excludes every key j > i from row i. Returns (O [nrows, D] f64, LSE [nrows] f64).
+    excludes every key j > i from row i. K, V (and ``v_scale`` [Hkv, D]) may hold
+    Hkv heads, a divisor of Q's H: query head h reads K/V head h // (H // Hkv).
+    Returns (O [nrows, D] f64, LSE [nrows] f64).
     """
     v = _c(v)
-    B, H, Sk, D = v.shape
+    B, Hkv, Sk, D = v.shape
     if qk is not None:
         q8 = _c(qk["q8"], np.int8)
         Sq = q8.shape[2]
@@ -182,6 +193,8 @@ def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | Non
         Sq = qf.shape[2]
         q8 = qs = k8 = ks = None
         qm = None
+    H = (q8 if q8 is not None else qf).shape[1]
+    _kv_heads(H, Hkv)
     if causal and Sq != Sk:
         raise ValueError("causal attention is defined here for self-attention (Sq == Sk)")
     base, b4, bdt, bsb, bsh, bsq, bsk = _bias_args(bias, B, H, Sq, Sk)
@@ -202,7 +215,7 @@ def attn(qk: dict | None, v: np.ndarray, sm_scale: float, *, q: np.ndarray | Non
     lse = np.empty(nrows, np.float64)
     # the bias pointer is the first element of the broadcast view (strides may be 0)
     bptr = None if b4 is None else ctypes.c_void_p(b4.__array_interface__["data"][0])
-    lib().oracle_attn(B, H, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(qf), _ptr(kf),
+    lib().oracle_attn(B, H, Hkv, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(qf), _ptr(kf),
                       _ptr(v), dtype_code(v), float(sm_scale), bptr, bdt, bsb, bsh, bsq, bsk,
                       _ptr(mask), _ptr(vbs), _ptr(v_scale), nseg, _ptr(seg), _ptr(qm), int(bool(causal)),
                       _ptr(rows), nrows, _ptr(o), _ptr(lse))

@@ -50,6 +50,10 @@
  *  R6 LSE is that of the uncentred scores: the centring shift
  *     -sm_scale*(q.mu) is added back as +sm_scale*qmu.
  *  R7 a fully excluded row gives O = 0 and LSE = -inf.
+ *  R8 grouped-query attention: H query heads share Hkv K/V heads (H a
+ *     multiple of Hkv), query head h reading K/V head h / (H/Hkv) (runs of
+ *     consecutive query heads per K/V head); K mean, K codes and the V scale
+ *     belong to the K/V head, and q.mu of a query row uses its K/V head's mean.
  *
  * Parity pins (tests/test_oracle_*.py): hand-worked quantization examples
  * (tests/golden/), exact-rational means, brute-force integer scores, the
@@ -166,15 +170,18 @@ void oracle_quantize_rows(const void* x, int dtype, int64_t B, int64_t H, int64_
 
 /* ---- step 3: centring term qmu_i = sum_c q_ic * mu_c (fp64) [reading R6] ---- */
 
-void oracle_qmu(const void* qx, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+/* qx: [B,H,S,D]; mean: [B,Hkv,D], the K mean of the K/V head query head h
+ * reads (h / (H/Hkv), reading R8); qmu: [B,H,S]. */
+void oracle_qmu(const void* qx, int dtype, int64_t B, int64_t H, int64_t Hkv, int64_t S, int64_t D,
                 const float* mean, const int32_t* vbs, double* qmu) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < B * H * S; ++r) {
         int64_t bh = r / S, j = r % S;
+        int64_t kvh = (bh / H) * Hkv + (bh % H) / (H / Hkv);
         double acc = 0.0;
         if (!is_pad_row(vbs, j))
             for (int64_t c = 0; c < D; ++c)
-                acc += (double)load_elem(qx, dtype, r * D + c) * (double)mean[bh * D + c];
+                acc += (double)load_elem(qx, dtype, r * D + c) * (double)mean[kvh * D + c];
         qmu[r] = acc;
     }
 }
@@ -207,21 +214,24 @@ void oracle_scores_i32(const int8_t* q8, const int8_t* k8, int64_t Sq, int64_t S
  * block mask drops its tile or it is a pad key of its tile, when its
  * bias is -inf, or (causal, self-attention: Sq = Sk) when j > i.
  *
+ * Query head h reads K/V head h / (H/Hkv) (grouped-query attention; Hkv = H
+ * is plain multi-head attention; reading R8).
+ *
  * Layouts (all contiguous except the bias, which takes element strides so
  * that a [1,1,1,K] stride-0 broadcast and its [B,H,Q,K] expansion are both
  * expressible):
- *   q8 [B,H,Sq,D] int8, qs [B,H,Sq], k8 [B,H,Sk,D] int8, ks [B,H,Sk]
- *   qf [B,H,Sq,D] f64, kf [B,H,Sk,D] f64 (no-quant mode)
- *   v  [B,H,Sk,D] of v_dtype
+ *   q8 [B,H,Sq,D] int8, qs [B,H,Sq], k8 [B,Hkv,Sk,D] int8, ks [B,Hkv,Sk]
+ *   qf [B,H,Sq,D] f64, kf [B,Hkv,Sk,D] f64 (no-quant mode)
+ *   v  [B,Hkv,Sk,D] of v_dtype
  *   bias (nullable) of bias_dtype, element (b,h,i,j) at
  *        b*bsb + h*bsh + i*bsq + j*bsk
  *   mask (nullable) [B,H,Sq/64,Sk/64] uint8, vbs [Sk/64] (nullable)
- *   v_scale (nullable) [H,D] fp32
+ *   v_scale (nullable) [Hkv,D] fp32, the scale of the stored V head
  *   seg: nseg pairs (start, len); nseg = 0 means the whole [0, Sk)
  *   qmu (nullable) [B,H,Sq] fp64, added as sm_scale*qmu to the LSE
  *   o [nrows, D] f64, lse [nrows] f64 (row order of `rows`)
  */
-void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+void oracle_attn(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                  const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
                  const double* qf, const double* kf,
                  const void* v, int v_dtype, float sm_scale,
@@ -235,6 +245,7 @@ void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
     for (int64_t n = 0; n < nrows; ++n) {
         int64_t r = rows ? rows[n] : n;
         int64_t bh = r / Sq, i = r % Sq, b = bh / H, h = bh % H;
+        int64_t hk = h / (H / Hkv), kvh = b * Hkv + hk;   /* the K/V head of query head h */
         double* s = (double*)malloc(sizeof(double) * (size_t)Sk);
         double m = -INFINITY;
         for (int64_t j = 0; j < Sk; ++j) {
@@ -252,11 +263,11 @@ void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                 if (q8) {
                     int32_t acc = 0;
                     for (int64_t c = 0; c < D; ++c)
-                        acc += (int32_t)q8[r * D + c] * (int32_t)k8[(bh * Sk + j) * D + c];
-                    dot = (double)qs[r] * (double)ks[bh * Sk + j] * (double)acc;
+                        acc += (int32_t)q8[r * D + c] * (int32_t)k8[(kvh * Sk + j) * D + c];
+                    dot = (double)qs[r] * (double)ks[kvh * Sk + j] * (double)acc;
                 } else {
                     dot = 0.0;
-                    for (int64_t c = 0; c < D; ++c) dot += qf[r * D + c] * kf[(bh * Sk + j) * D + c];
+                    for (int64_t c = 0; c < D; ++c) dot += qf[r * D + c] * kf[(kvh * Sk + j) * D + c];
                 }
                 sij = (double)sm_scale * dot;
                 if (bias) sij += (double)load_elem(bias, bias_dtype, b * bsb + h * bsh + i * bsq + j * bsk);
@@ -275,11 +286,11 @@ void oracle_attn(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                 double p = exp(s[j] - m);
                 l += p;
                 for (int64_t c = 0; c < D; ++c)
-                    orow[c] += p * (double)load_elem(v, v_dtype, (bh * Sk + j) * D + c);
+                    orow[c] += p * (double)load_elem(v, v_dtype, (kvh * Sk + j) * D + c);
             }
             for (int64_t c = 0; c < D; ++c) {
                 orow[c] /= l;
-                if (v_scale) orow[c] *= (double)v_scale[h * D + c];
+                if (v_scale) orow[c] *= (double)v_scale[hk * D + c];
             }
             lse[n] = m + log(l) + (qmu ? (double)sm_scale * qmu[r] : 0.0);
         }

@@ -16,12 +16,18 @@ import workloads as W
 
 
 def _sdpa64(q, k, v, scale, mask=None, is_causal=False):
-    """fp64 CPU SDPA and its log-sum-exp, the library reference for no-quant attention."""
+    """fp64 CPU SDPA and its log-sum-exp, the library reference for no-quant attention. K/V with
+    fewer heads than Q use torch's grouped-query mode (``enable_gqa``), and the log-sum-exp
+    reads K through ``repeat_interleave``, torch's statement of the same head grouping."""
     qt = torch.tensor(W.to_f32(q), dtype=torch.float64)
     kt = torch.tensor(W.to_f32(k), dtype=torch.float64)
     vt = torch.tensor(W.to_f32(v), dtype=torch.float64)
     m = None if mask is None else torch.tensor(mask, dtype=torch.float64)
-    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale, is_causal=is_causal)
+    gqa = kt.shape[1] != qt.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale, is_causal=is_causal,
+                                                         enable_gqa=gqa)
+    if gqa:
+        kt = kt.repeat_interleave(qt.shape[1] // kt.shape[1], dim=1)
     s = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
     if m is not None:
         s = s + m
@@ -51,6 +57,45 @@ def test_noquant_causal_matches_sdpa(oracle_lib):
     ro, rl = _sdpa64(q, k, v, w.sm_scale, is_causal=True)
     assert np.max(np.abs(o - ro.reshape(-1, 128))) < 1e-12
     assert np.max(np.abs(lse - rl.reshape(-1))) < 1e-12
+
+
+@pytest.mark.parametrize("hkv,causal", [(2, False), (1, False), (2, True)])
+def test_noquant_gqa_matches_sdpa(oracle_lib, hkv, causal):
+    # grouped-query attention: 4 query heads over hkv K/V heads, head h reading K/V head
+    # h // (4 // hkv), against torch's SDPA in its grouped-query mode
+    w = W.WORKLOADS["tiny"]
+    q, k, v = W.make_qkv(w, H=4, Hkv=hkv, Sq=160, Sk=160)
+    assert k.shape[1] == hkv and v.shape[1] == hkv
+    o, lse = oracle_lib.attn(None, v, w.sm_scale, q=W.to_f32(q), k=W.to_f32(k), causal=causal)
+    ro, rl = _sdpa64(q, k, v, w.sm_scale, is_causal=causal)
+    assert np.max(np.abs(o - ro.reshape(-1, 128))) < 1e-12
+    assert np.max(np.abs(lse - rl.reshape(-1))) < 1e-12
+
+
+def test_quantized_gqa_equals_repeated_kv(oracle_lib):
+    # quantized mode: K/V heads shared by runs of query heads give exactly what multi-head
+    # attention gives on K/V (and V scale) repeated per query head: the K mean and K codes are
+    # per K/V head, and each query row's centring term uses its K/V head's mean
+    w = W.WORKLOADS["dense4k"]          # per-channel K offset: a nonzero mean per K/V head
+    H, hkv, S = 6, 2, 200
+    q, k, v = W.make_qkv(w, H=H, Hkv=hkv, Sq=S, Sk=S)
+    g = H // hkv
+    k_rep, v_rep = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    vsc = W.v_scale(w, H=hkv)
+    qk = oracle_lib.quantize_qk(q, k)
+    qk_rep = oracle_lib.quantize_qk(q, k_rep)
+    for name in ("k8", "ks", "kmean"):
+        assert np.array_equal(np.repeat(qk[name], g, axis=1), qk_rep[name]), name
+    for name in ("q8", "qs", "qmu"):
+        assert np.array_equal(qk[name], qk_rep[name]), name
+    bias = W.bias_tensor(W.band_bias(S, core=(40, 120), skirt=40), "fp32")
+    for causal in (False, True):
+        o, l = oracle_lib.attn(qk, v, w.sm_scale, bias=bias, v_scale=vsc, causal=causal)
+        o_r, l_r = oracle_lib.attn(qk_rep, v_rep, w.sm_scale, bias=bias, v_scale=np.repeat(vsc, g, axis=0),
+                                   causal=causal)
+        assert np.array_equal(o, o_r) and np.array_equal(l, l_r)
+    with pytest.raises(ValueError):
+        oracle_lib.attn(qk, v[:, :1].repeat(4, axis=1), w.sm_scale)   # 6 query heads over 4
 
 
 def test_causal_equals_triangular_bias(oracle_lib):

@@ -27,6 +27,9 @@ same shapes stand in for them):
              attends key tiles u < 8 (prefix) or |u - t| <= 48 (band), the same
              for every head; validity vector 64 everywhere except 17 in the
              last tile, pad rows of Q/K/V zero; V scale [H,D] ~ U(0.5, 2).
+  * gqa:     B2 S2048 H16 Hkv2 D128 bf16, causal self-attention: the
+             grouped-query shape of ROCm/FlyDSL PR #886's timed table (runs
+             of 8 query heads share one K/V head).
 """
 from __future__ import annotations
 
@@ -95,17 +98,20 @@ WORKLOADS = {
                      extras={"core": (6720, 20160), "skirt": 6720}),
     "sparse": Workload("sparse", 5, 1, 24, 131072, 131072, 128, "bf16",
                        extras={"prefix": 8, "band": 48, "last_valid": 17}),
+    "gqa": Workload("gqa", 6, 2, 16, 2048, 2048, 128, "bf16", extras={"hkv": 2, "causal": True}),
 }
 
 
-def make_qkv(w: Workload, B=None, H=None, Sq=None, Sk=None):
+def make_qkv(w: Workload, B=None, H=None, Sq=None, Sk=None, Hkv=None):
     """Q, K, V of the workload (optionally with smaller B/H/Sq/Sk for parity tests).
 
-    A smaller draw uses the same recipe and seeds, so its values differ from
-    a slice of the full-size draw; it is a workload of the same kind.
+    K and V hold Hkv heads (the workload's "hkv", else H). A smaller draw
+    uses the same recipe and seeds, so its values differ from a slice of the
+    full-size draw; it is a workload of the same kind.
     """
     B = B or w.B
     H = H or w.H
+    Hkv = Hkv or w.extras.get("hkv", H)
     Sq = Sq or w.Sq
     Sk = Sk or w.Sk
     offset = None
@@ -113,8 +119,8 @@ def make_qkv(w: Workload, B=None, H=None, Sq=None, Sk=None):
         offset = rng(w.cfg_id, KOFF_ID).standard_normal(size=(w.D,), dtype=np.float32) * np.float32(
             w.extras["k_offset_std"])
     q = normal(w.cfg_id, Q_ID, (B, H, Sq, w.D), w.dtype)
-    k = normal(w.cfg_id, K_ID, (B, H, Sk, w.D), w.dtype, offset=offset)
-    v = normal(w.cfg_id, V_ID, (B, H, Sk, w.D), w.dtype)
+    k = normal(w.cfg_id, K_ID, (B, Hkv, Sk, w.D), w.dtype, offset=offset)
+    v = normal(w.cfg_id, V_ID, (B, Hkv, Sk, w.D), w.dtype)
     return q, k, v
 
 
