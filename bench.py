@@ -410,6 +410,35 @@ def other_configs(dev) -> int:
         del q, k, v, qk, out, lse, ws
         torch.cuda.empty_cache()
 
+    # the causal shapes of ROCm/FlyDSL PR #886's timed table, (B, S, H, Hkv, D) and its FlyDSL
+    # +LSE latency in us (bf16 QK on an MI350X: context, not a target); TFLOPS as that table
+    # counts them, half of 4*B*H*S*S*D
+    flydsl = [((2, 2048, 16, 16, 128), 51.3), ((2, 4096, 16, 16, 128), 154.7), ((1, 8192, 16, 16, 128), 262.8),
+              ((2, 2048, 16, 2, 128), 50.4), ((4, 2048, 8, 8, 64), 38.7), ((8, 1024, 16, 16, 128), 58.5)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(886)
+    rows = []
+    for (B, S, H, Hkv, D), page_us in flydsl:
+        q = torch.randn((B, H, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
+        ws = torch.empty(qfa.quantize_workspace_bytes(B, Hkv, S, D), dtype=torch.uint8, device=dev)
+        qk = qfa.quantize_qk(q, k, workspace=ws)
+        out = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        scale = D ** -0.5
+        t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
+        t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, scale, causal=True, out=out, lse=lse), 20)
+        fl = 4.0 * B * H * S * S * D / 2
+        rows.append({"shape": f"B{B} S{S} H{H} Hkv{Hkv} D{D}", "quantize_us": round(t_q * 1e3, 1),
+                     "attn_us": round(t_a * 1e3, 1), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
+                     "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
+                     "end_to_end_us": round((t_q + t_a) * 1e3, 1), "page_flydsl_lse_us": page_us})
+        del q, k, v, ws, qk, out, lse
+    torch.cuda.empty_cache()
+    print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V, int8 QK",
+                      "rows": rows, "device": info}), flush=True)
+
     # the banded workload with the pages' bool [1,1,1,K] keep mask (raised-cosine weight > 1e-3)
     w = W.WORKLOADS["band"]
     q_np, k_np, v_np = W.make_qkv(w)

@@ -70,7 +70,8 @@ const char* qfa_last_error(void);
 
 /*
  * qfa_quantize_workspace_bytes — device workspace qfa_quantize_qk needs for
- * the K mean (fp64 partial sums). Writes the byte count to *bytes.
+ * the K mean (fp64 partial sums). H is K's head count (Hkv of a
+ * grouped-query call). Writes the byte count to *bytes.
  */
 int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, size_t* bytes);
 
@@ -85,27 +86,31 @@ int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, si
  *   a < 127*FLT_MIN  -> codes 0, scale 0;
  *   else scale = fp32(a / 127), inv = fp32(127 / a),
  *        code_c = clamp(round_half_even(fp32(x_c * inv)), -127, 127).
- * mu[b,h,c] = fp32( fp64( exact sum over valid keys of K[b,h,j,c] ) / n ),
+ * mu[b,g,c] = fp32( fp64( exact sum over valid keys of K[b,g,j,c] ) / n ),
  * n = Sk, or max(1, sum(vbs)) when vbs is given; K - mu is one fp32
- * subtraction. qmu[b,h,i] = sum_c Q[b,h,i,c]*mu[b,h,c] (fp32) lets attn_fwd
- * report the LSE of the uncentred scores.
+ * subtraction. qmu[b,h,i] = sum_c Q[b,h,i,c]*mu[b,h/(H/Hkv),c] (fp32) lets
+ * attn_fwd report the LSE of the uncentred scores.
  *
- * q, k:    [B,H,Sq,D] / [B,H,Sk,D] of `dtype` (QFA_BF16 or QFA_FP16), strides
- *          as above; base and row strides 16-byte aligned.
+ * H, Hkv:  heads of Q and of K. Hkv divides H; Hkv < H is grouped-query
+ *          attention (ROCm/FlyDSL PR #886 tests and times "MHA and GQA"):
+ *          query head h shares K/V head h / (H/Hkv) with the other query
+ *          heads of its run. Hkv == H is multi-head attention.
+ * q, k:    [B,H,Sq,D] / [B,Hkv,Sk,D] of `dtype` (QFA_BF16 or QFA_FP16),
+ *          strides as above; base and row strides 16-byte aligned.
  * vbs:     nullable; int32[Sk/64] per-tile valid-token counts in [0,64]
  *          (requires Sq == Sk, a multiple of 64). Pad rows (j mod 64 >=
  *          vbs[j/64]) of Q and K get codes 0 and scale 0 and are left out of
  *          the mean.
  * center_k: 0 = no centring (kmean, qmu unused and may be NULL).
- * q8, k8:  int8 [B,H,Sq,D] / [B,H,Sk,D] contiguous outputs.
- * qs, ks:  fp32 [B,H,Sq] / [B,H,Sk] contiguous outputs.
- * kmean:   fp32 [B,H,D] output (required when center_k).
+ * q8, k8:  int8 [B,H,Sq,D] / [B,Hkv,Sk,D] contiguous outputs.
+ * qs, ks:  fp32 [B,H,Sq] / [B,Hkv,Sk] contiguous outputs.
+ * kmean:   fp32 [B,Hkv,D] output (required when center_k).
  * qmu:     nullable fp32 [B,H,Sq] output (only when center_k).
- * workspace: device buffer of at least qfa_quantize_workspace_bytes(...)
- *          bytes, 16-byte aligned (may be NULL when center_k == 0).
+ * workspace: device buffer of at least qfa_quantize_workspace_bytes(B,
+ *          Hkv, Sk, D) bytes, 16-byte aligned (may be NULL when center_k == 0).
  * D must be 64 or 128.
  */
-int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
                     const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
                     const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
                     const int32_t* vbs, int center_k,
@@ -141,11 +146,13 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * a bias of -inf also excludes it. A row with no attended key gives O = 0 and
  * LSE = -inf.
  *
+ * H, Hkv:  heads of Q and of K/V; Hkv divides H, and query head h reads K/V
+ *           head h / (H/Hkv) (grouped-query attention when Hkv < H).
  * q8, qs:   int8 [B,H,Sq,D], fp32 [B,H,Sq] (from qfa_quantize_qk).
  * qmu:      nullable fp32 [B,H,Sq]; when given, sm_scale*qmu is added to the
  *           LSE (pass it whenever K was centred and the LSE is requested).
- * k8, ks:   int8 [B,H,Sk,D], fp32 [B,H,Sk].
- * v:        [B,H,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
+ * k8, ks:   int8 [B,Hkv,Sk,D], fp32 [B,Hkv,Sk].
+ * v:        [B,Hkv,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
  *           v_sh, v_ss); base and row strides 16-byte aligned; v_ss below
  *           2^24 elements (else QFA_ERR_UNSUPPORTED).
  * sm_scale: softmax scale (typically D^-0.5).
@@ -165,7 +172,7 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  *           in [0, T), as qfa_blockmask_to_index writes them (the kernel
  *           merges the lists of neighbouring query tiles); other lists give
  *           unspecified results, with every access still in bounds.
- * v_scale:  nullable fp32 [H,D] per-(head,channel) factor applied to O.
+ * v_scale:  nullable fp32 [Hkv,D] per-(V head, channel) factor applied to O.
  * nseg, seg: host array of nseg (<= 4) (start, length) pairs of key ranges,
  *           ascending and disjoint; nseg = 0 means the whole [0, Sk).
  * causal:   nonzero: causal self-attention, row i attends keys j <= i only
@@ -180,7 +187,7 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * lse:      nullable fp32 [B,H,Sq] contiguous output; non-NULL requests it.
  * D must be 64 or 128.
  */
-int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                  const int8_t* q8, const float* qs, const float* qmu,
                  const int8_t* k8, const float* ks,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,

@@ -70,28 +70,30 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = Non
                 workspace: torch.Tensor | None = None) -> dict:
     """Per-token symmetric int8 Q/K (+ K mean, centring term) on the GPU.
 
+    K may hold fewer heads than Q (grouped-query attention: query head h shares K/V head
+    h // (H // Hkv)); the K outputs then have Hkv heads.
     Returns dict(q8, qs, k8, ks, kmean, qmu); kmean/qmu are None when center_k is False.
     """
     _no_grad(q, k)
     B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or k.dtype != q.dtype:
-        raise ValueError("q and k must agree in B, H, D and dtype")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or k.dtype != q.dtype:
+        raise ValueError("q and k must agree in B, D and dtype")
     dq, *qst = _view(q, "q")
     _, *kst = _view(k, "k")
     dev = q.device
     vbs = _cont(vbs, "vbs", torch.int32)
     q8 = torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev)
-    k8 = torch.empty((B, H, Sk, D), dtype=torch.int8, device=dev)
+    k8 = torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev)
     qs = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    ks = torch.empty((B, H, Sk), dtype=torch.float32, device=dev)
-    kmean = torch.empty((B, H, D), dtype=torch.float32, device=dev) if center_k else None
+    ks = torch.empty((B, Hkv, Sk), dtype=torch.float32, device=dev)
+    kmean = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if center_k else None
     qmu = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if center_k else None
-    nbytes = quantize_workspace_bytes(B, H, Sk, D) if center_k else 0
+    nbytes = quantize_workspace_bytes(B, Hkv, Sk, D) if center_k else 0
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().qfa_quantize_qk(
-        B, H, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
+        B, H, Hkv, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
         _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(kmean), _ptr(qmu),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev)))
     return dict(q8=q8, qs=qs, k8=k8, ks=ks, kmean=kmean, qmu=qmu)
@@ -129,6 +131,11 @@ def qk_scores_i32(q8: torch.Tensor, k8: torch.Tensor) -> torch.Tensor:
     return s32
 
 
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+
+
 def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,
              index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
              v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
@@ -144,13 +151,22 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
     segments: up to 4 ascending disjoint (start, length) key ranges.
     causal: self-attention (Sq == Sk) where row i attends keys j <= i only.
     return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
+    K/V may hold Hkv heads, a divisor of H (grouped-query attention; ``qk`` from
+    :func:`quantize_qk` with such a K): query head h reads K/V head h // (H // Hkv), and
+    ``v_scale`` is [Hkv, D].
     """
     _no_grad(v, bias)
     q8, qs, k8, ks, qmu = qk["q8"], qk["qs"], qk["k8"], qk["ks"], qk.get("qmu")
     B, H, Sq, D = q8.shape
-    Sk = k8.shape[2]
-    if v.shape != (B, H, Sk, D):
-        raise ValueError(f"v shape {tuple(v.shape)} != {(B, H, Sk, D)}")
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    if v.shape != (B, Hkv, Sk, D):
+        raise ValueError(f"v shape {tuple(v.shape)} != {(B, Hkv, Sk, D)}")
+    _shape(k8, "k8", (B, Hkv, Sk, D)), _shape(qs, "qs", (B, H, Sq)), _shape(ks, "ks", (B, Hkv, Sk))
+    _shape(qmu, "qmu", (B, H, Sq)), _shape(v_scale, "v_scale", (Hkv, D))
+    _shape(out, "out", (B, H, Sq, D)), _shape(lse, "lse", (B, H, Sq))
+    if index is not None:
+        T = Sk // 64
+        _shape(index, "index", (B, H, T, T)), _shape(count, "count", (B, H, T)), _shape(vbs, "vbs", (T,))
     _cont(q8, "q8", torch.int8), _cont(k8, "k8", torch.int8)
     _cont(qs, "qs", torch.float32), _cont(ks, "ks", torch.float32), _cont(qmu, "qmu", torch.float32)
     dv, *vst = _view(v, "v")
@@ -185,7 +201,7 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
         nseg = len(segs) // 2
         seg = (ctypes.c_int64 * max(1, len(segs)))(*segs)
     _lib.check(_lib.lib().qfa_attn_fwd(
-        B, H, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
+        B, H, Hkv, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
         _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
         bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
         int(bool(causal)), _ptr(out), do, *ost, _ptr(lse), _stream(dev)))

@@ -47,12 +47,12 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_last_error.restype = ctypes.c_char_p
     L.qfa_quantize_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]
     L.qfa_quantize_workspace_bytes.restype = _I
-    L.qfa_quantize_qk.argtypes = ([_I64] * 5 + [_I] + [_P, _I64, _I64, _I64] * 2
+    L.qfa_quantize_qk.argtypes = ([_I64] * 6 + [_I] + [_P, _I64, _I64, _I64] * 2
                                   + [_P, _I] + [_P] * 6 + [_P, ctypes.c_size_t, _P])
     L.qfa_quantize_qk.restype = _I
     L.qfa_blockmask_to_index.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.qfa_blockmask_to_index.restype = _I
-    L.qfa_attn_fwd.argtypes = ([_I64] * 5 + [_P] * 5 + [_P, _I, _I64, _I64, _I64] + [ctypes.c_float]
+    L.qfa_attn_fwd.argtypes = ([_I64] * 6 + [_P] * 5 + [_P, _I, _I64, _I64, _I64] + [ctypes.c_float]
                                + [_P, _I, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
                                + [_P, _I, _I64, _I64, _I64] + [_P, _P])
     L.qfa_attn_fwd.restype = _I

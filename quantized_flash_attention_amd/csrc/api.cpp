@@ -55,6 +55,16 @@ int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
   return QFA_OK;
 }
 
+// Hkv K/V heads shared by runs of H / Hkv query heads
+int check_kv_heads(int64_t H, int64_t Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv) {
+    if (H == 0 && Hkv == 0) return QFA_OK;
+    return fail(QFA_ERR_INVALID_ARG, "%lld query heads cannot share %lld K/V heads (Hkv must divide H)",
+                (long long)H, (long long)Hkv);
+  }
+  return QFA_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(QFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -64,7 +74,7 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-int qfa_version(void) { return 100; }
+int qfa_version(void) { return 200; }
 
 const char* qfa_status_string(int status) {
   switch (status) {
@@ -86,7 +96,7 @@ int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, si
   return ok();
 }
 
-int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
                     const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
                     const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
                     const int32_t* vbs, int center_k,
@@ -94,6 +104,7 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int
                     void* workspace, size_t workspace_bytes, void* stream) {
   int st;
   if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if ((st = check_kv_heads(H, Hkv))) return st;
   if (dtype != QFA_BF16 && dtype != QFA_FP16)
     return fail(dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "Q/K dtype %d (supported: bf16, fp16)", dtype);
   if (B * H == 0) return ok();  // nothing to read or write: empty tensors may have NULL data
@@ -112,26 +123,26 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, int
     if (!kmean) return fail(QFA_ERR_INVALID_ARG, "kmean output is NULL with center_k");
     if (!aligned16(kmean) || (qmu && !aligned16(qmu))) return fail(QFA_ERR_INVALID_ARG, "kmean/qmu must be 16-byte aligned");
     size_t need = 0;
-    qfa_quantize_workspace_bytes(B, H, Sk, D, &need);
+    qfa_quantize_workspace_bytes(B, Hkv, Sk, D, &need);
     if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
       return fail(QFA_ERR_INVALID_ARG, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   }
   hipStream_t s = (hipStream_t)stream;
   if (center_k && Sk > 0) {
-    qfa::MeanArgs m{k, dtype, B, H, Sk, D, k_sb, k_sh, k_ss, vbs, (double2*)workspace, kmean,
+    qfa::MeanArgs m{k, dtype, B, Hkv, Sk, D, k_sb, k_sh, k_ss, vbs, (double2*)workspace, kmean,
                     (int)((Sk + qfa::kMeanChunkRows - 1) / qfa::kMeanChunkRows)};
     if ((st = hip_status(qfa::launch_kmean(m, s), "kmean launch"))) return st;
   } else if (center_k) {
-    if ((st = hip_status(qfa::launch_zero_words(kmean, B * H * D, s), "kmean clear"))) return st;
+    if ((st = hip_status(qfa::launch_zero_words(kmean, B * Hkv * D, s), "kmean clear"))) return st;
   }
   if (Sq > 0) {
     qfa::QuantRowsArgs qa{q, dtype, B, H, Sq, D, q_sb, q_sh, q_ss, nullptr,
-                          center_k ? kmean : nullptr, vbs, q8, qs, center_k ? qmu : nullptr};
+                          center_k ? kmean : nullptr, Hkv, vbs, q8, qs, center_k ? qmu : nullptr};
     if ((st = hip_status(qfa::launch_quantize_rows(qa, s), "quantize Q launch"))) return st;
   }
   if (Sk > 0) {
-    qfa::QuantRowsArgs ka{k, dtype, B, H, Sk, D, k_sb, k_sh, k_ss, center_k ? kmean : nullptr,
-                          nullptr, vbs, k8, ks, nullptr};
+    qfa::QuantRowsArgs ka{k, dtype, B, Hkv, Sk, D, k_sb, k_sh, k_ss, center_k ? kmean : nullptr,
+                          nullptr, Hkv, vbs, k8, ks, nullptr};
     if ((st = hip_status(qfa::launch_quantize_rows(ka, s), "quantize K launch"))) return st;
   }
   return ok();
@@ -152,7 +163,7 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
                     "blockmask_to_index launch");
 }
 
-int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                  const int8_t* q8, const float* qs, const float* qmu,
                  const int8_t* k8, const float* ks,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
@@ -164,6 +175,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  float* lse, void* stream) {
   int st;
   if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if ((st = check_kv_heads(H, Hkv))) return st;
   if (v_dtype != QFA_BF16 && v_dtype != QFA_FP16)
     return fail(v_dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "V dtype %d (supported: bf16, fp16)", v_dtype);
   if (B * H * Sq == 0) return ok();  // no output rows: empty tensors may have NULL data
@@ -222,7 +234,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
   }
   a.nseg = nseg;
   a.causal = causal ? 1 : 0;
-  a.B = (int)B; a.H = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
+  a.B = (int)B; a.H = (int)H; a.Hkv = (int)Hkv; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
   a.q8 = q8; a.qs = qs; a.qmu = qmu; a.k8 = k8; a.ks = ks;
   a.v = v; a.v_dtype = v_dtype; a.v_sb = v_sb; a.v_sh = v_sh; a.v_ss = v_ss;
   a.sm_scale = sm_scale;
@@ -244,7 +256,7 @@ int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
     return fail(QFA_ERR_INVALID_ARG, "q8, k8 and s32 must be 16-byte aligned");
   if (B * H * Sq * Sk > (1ll << 40)) return fail(QFA_ERR_UNSUPPORTED, "score tensor too large");
   qfa::AttnArgs a{};
-  a.B = (int)B; a.H = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
+  a.B = (int)B; a.H = (int)H; a.Hkv = (int)H; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
   a.q8 = q8; a.k8 = k8;
   a.nseg = 1;
   a.seg_lo[0] = 0;

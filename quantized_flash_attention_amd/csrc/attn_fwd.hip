@@ -277,7 +277,8 @@ __device__ __forceinline__ void stage_barrier() {
 // (-inf for a row with no attended key, whose O is 0).
 template <int D, bool LSE>
 __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D / 32], const float (&lsum)[4],
-                                           float m_run, int b, int h, int q, int64_t qrow, bool qvalid, int hl) {
+                                           float m_run, int b, int h, int hk, int q, int64_t qrow, bool qvalid,
+                                           int hl) {
   const float l_tot = xsum32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
   if (!qvalid) return;
   const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -291,7 +292,7 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 #pragma unroll
       for (int r = 0; r < 4; ++r) vals[r] = o[c][4 * g + r] * inv_l;
       if (a.v_scale) {
-        const float4 vs = *(const float4*)(a.v_scale + (int64_t)h * D + d0);
+        const float4 vs = *(const float4*)(a.v_scale + (int64_t)hk * D + d0);   // the V head's scale
         vals[0] *= vs.x; vals[1] *= vs.y; vals[2] *= vs.z; vals[3] *= vs.w;
       }
       if (a.out_dtype == FP32) {
@@ -458,11 +459,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // either way)
   const float crow = DUMP ? 1.0f : fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f);
 
-  // ---- per-(b,h) sources; every copy and load is range-checked ----
-  const unsigned char* kbase = (const unsigned char*)(a.k8 + (int64_t)bh * a.Sk * D);
-  const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * 2;
+  // ---- per-(b,h) sources; every copy and load is range-checked. K8, key
+  // scales and V come from the K/V head of this query head (grouped-query
+  // calls share one among H / Hkv consecutive query heads) ----
+  const int hk = h / (a.H / a.Hkv);
+  const int64_t bhk = (int64_t)b * a.Hkv + hk;
+  const unsigned char* kbase = (const unsigned char*)(a.k8 + bhk * a.Sk * D);
+  const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh) * 2;
   const int v_row = (int)(a.v_ss * 2);   // below 2^25 (checked by the caller)
-  const float* ksbase = a.ks + (int64_t)bh * a.Sk;
+  const float* ksbase = a.ks + bhk * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
   // unbiased instances take a [1,1,1,K] keep mask (bool bytes) through the
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // drain this wave's remaining copies (they target stages nobody reads)
   wait_vmcnt<0>();
 
-  if constexpr (!DUMP) store_rows<D, LSE>(a, o, lsum, m_run, b, h, q, qrow, qvalid, hl);
+  if constexpr (!DUMP) store_rows<D, LSE>(a, o, lsum, m_run, b, h, hk, q, qrow, qvalid, hl);
 }
 
 

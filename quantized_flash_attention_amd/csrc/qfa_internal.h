@@ -29,8 +29,9 @@ struct QuantRowsArgs {
   int dtype;
   int64_t B, H, S, D;
   int64_t sb, sh, ss;
-  const float* mean;    // nullable: centre rows by mean[bh, :]
-  const float* qmu_mean;// nullable: compute qmu = x . qmu_mean[bh, :] into qmu
+  const float* mean;    // nullable: centre rows by mean[b, h / (H / mean_heads), :]
+  const float* qmu_mean;// nullable: compute qmu = x . qmu_mean[b, h / (H / mean_heads), :] into qmu
+  int64_t mean_heads;   // heads of mean / qmu_mean (K's heads; divides H)
   const int32_t* vbs;   // nullable
   int8_t* codes;        // [B*H*S, D]
   float* scale;         // [B*H*S]
@@ -46,7 +47,7 @@ hipError_t launch_blockmask_to_index(const uint8_t* mask, int64_t rows, int64_t 
                                      int32_t* count, hipStream_t s);
 
 struct AttnArgs {
-  int B, H, Sq, Sk, D;
+  int B, H, Hkv, Sq, Sk, D;   // query head h reads K/V head h / (H / Hkv)
   const int8_t* q8;
   const float* qs;
   const float* qmu;     // nullable
@@ -62,7 +63,7 @@ struct AttnArgs {
   const int32_t* index; // nullable (dense)
   const int32_t* count;
   const int32_t* vbs;   // nullable
-  const float* v_scale; // nullable [H, D]
+  const float* v_scale; // nullable [Hkv, D]
   int nseg;
   int seg_lo[4], seg_hi[4];
   int causal;           // self-attention with key j > row i excluded (Sq == Sk, one segment [0, Sk))

@@ -124,6 +124,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   if (r >= rows) return;  // whole row groups leave together (G divides 64)
   const int64_t bh = r / a.S, j = r % a.S;
   const int64_t b = bh / a.H, h = bh % a.H;
+  // the mean row of this row's K/V head (grouped-query: runs of H / mean_heads heads share one)
+  const int64_t mrow = b * a.mean_heads + (int)h / (int)(a.H / a.mean_heads);
 
   const bool pad = is_pad(a.vbs, j);
   float x[8];
@@ -137,15 +139,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
 
   float qmu = 0.0f;
   if (a.qmu_mean) {
-    const float4 m0 = *(const float4*)(a.qmu_mean + bh * D + cg * 8);
-    const float4 m1 = *(const float4*)(a.qmu_mean + bh * D + cg * 8 + 4);
+    const float4 m0 = *(const float4*)(a.qmu_mean + mrow * D + cg * 8);
+    const float4 m1 = *(const float4*)(a.qmu_mean + mrow * D + cg * 8 + 4);
     const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) qmu += x[i] * mm[i];
   }
   if (a.mean) {
-    const float4 m0 = *(const float4*)(a.mean + bh * D + cg * 8);
-    const float4 m1 = *(const float4*)(a.mean + bh * D + cg * 8 + 4);
+    const float4 m0 = *(const float4*)(a.mean + mrow * D + cg * 8);
+    const float4 m1 = *(const float4*)(a.mean + mrow * D + cg * 8 + 4);
     const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = __fsub_rn(x[i], mm[i]);  // one fp32 subtraction

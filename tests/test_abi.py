@@ -42,8 +42,9 @@ def _quant(**kw):
     a = dict(B=1, H=2, Sq=128, Sk=128, D=128, dtype=1, q=FAKE, q_s=(32768, 16384, 128), k=FAKE,
              k_s=(32768, 16384, 128), vbs=None, center=1, outs=[FAKE] * 6, ws=FAKE, wsb=1 << 20)
     a.update(kw)
-    return _lib.lib().qfa_quantize_qk(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["dtype"], a["q"], *a["q_s"],
-                                      a["k"], *a["k_s"], a["vbs"], a["center"], *a["outs"], a["ws"], a["wsb"], None)
+    return _lib.lib().qfa_quantize_qk(a["B"], a["H"], a.get("Hkv", a["H"]), a["Sq"], a["Sk"], a["D"], a["dtype"],
+                                      a["q"], *a["q_s"], a["k"], *a["k_s"], a["vbs"], a["center"], *a["outs"],
+                                      a["ws"], a["wsb"], None)
 
 
 def test_quantize_rejects_bad_arguments():
@@ -59,6 +60,8 @@ def test_quantize_rejects_bad_arguments():
     assert _quant(wsb=16) == _lib.QFA_ERR_INVALID_ARG
     assert _quant(outs=[FAKE, FAKE, FAKE, FAKE, None, FAKE]) == _lib.QFA_ERR_INVALID_ARG  # kmean with center_k
     assert _quant(B=-1) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(Hkv=3) == _lib.QFA_ERR_INVALID_ARG
+    assert _quant(Hkv=0) == _lib.QFA_ERR_INVALID_ARG
 
 
 def _attn(**kw):
@@ -66,7 +69,7 @@ def _attn(**kw):
              bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None, causal=0,
              out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
     a.update(kw)
-    return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
+    return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a.get("Hkv", a["H"]), a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
                                    ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a["index"],
                                    a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["causal"], a["out"], a["odt"],
                                    *a["o_s"], a["lse"], None)
@@ -102,6 +105,10 @@ def test_attn_rejects_bad_arguments():
     assert b"Sq == Sk" in _lib.lib().qfa_last_error()
     assert _attn(causal=1, nseg=1, seg=_segs((0, 128))) == _lib.QFA_ERR_UNSUPPORTED
     assert _attn(causal=1, index=FAKE, count=FAKE) == _lib.QFA_ERR_UNSUPPORTED
+    # grouped-query heads: Hkv must divide H
+    for hkv in (0, 3, 4, -1):
+        assert _attn(Hkv=hkv) == _lib.QFA_ERR_INVALID_ARG
+    assert b"K/V heads" in _lib.lib().qfa_last_error()
 
 
 def test_merge_rejects_bad_arguments():

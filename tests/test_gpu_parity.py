@@ -309,6 +309,65 @@ def test_causal_full_size_sampled():
     check_lse(l, l_ref, rows, "causal full")
 
 
+GQA_CASES = {
+    # (workload, B, H, Hkv, Sq, Sk, options): runs of H / Hkv query heads share a K/V head
+    "h4_kv2": ("dense4k", 1, 4, 2, 300, 517, {}),
+    "h6_kv1_bias": ("band", 1, 6, 1, 200, 700, {"bias": True}),
+    "b2_h4_kv2_causal": ("dense4k", 2, 4, 2, 333, 333, {"causal": True}),
+    "h8_kv2_d64_fp16_vscale": ("d64", 1, 8, 2, 130, 260, {"vscale": True}),
+}
+
+
+@pytest.mark.parametrize("case", list(GQA_CASES))
+def test_gqa_parity(case):
+    """Grouped-query attention: quantization bit-exact (K mean and codes per K/V head, q.mu
+    from the group's mean) and attention against the oracle, with and without the LSE."""
+    wn, B, H, Hkv, Sq, Sk, opt = GQA_CASES[case]
+    w = W.WORKLOADS[wn]
+    q, k, v = W.make_qkv(w, B=B, H=H, Hkv=Hkv, Sq=Sq, Sk=Sk)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    assert g["k8"].shape[1] == Hkv and g["kmean"].shape[1] == Hkv
+    assert_quant_equal(g, ref)
+    bias = W.bias_tensor(W.band_bias(Sk, core=(Sk // 5, Sk - 2 * (Sk // 5)), skirt=Sk // 5), "fp32") \
+        if opt.get("bias") else None
+    vsc = W.v_scale(w, H=Hkv) if opt.get("vscale") else None
+    causal = opt.get("causal", False)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, v_scale=vsc, causal=causal)
+    kw = dict(bias=None if bias is None else up(bias), v_scale=None if vsc is None else up(vsc), causal=causal)
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, **kw)
+    check_o(o, o_ref, what=case)
+    check_lse(l, l_ref, what=case)
+    o2 = qfa.attn_fwd(g, up(v), w.sm_scale, **kw)
+    check_o(o2, o_ref, what=case + " no LSE")
+
+
+def test_gqa_sparse():
+    """Block-sparse with 4 query heads over 2 K/V heads: per-query-head tile lists."""
+    T, H = 6, 4
+    rs = np.random.default_rng(3)
+    mask = rs.random((1, H, T, T)) < 0.5
+    mask[..., 0] = True
+    vbs = np.array([64, 64, 30, 64, 64, 17], np.int32)
+    o, l, o_ref, l_ref = _sparse_case(T, H, mask, vbs, Hkv=2)
+    check_o(o, o_ref, what="gqa sparse")
+    check_lse(l, l_ref, what="gqa sparse")
+
+
+def test_gqa_full_size_sampled():
+    """B2 S2048 H16 Hkv2 D128 causal (the grouped-query shape of the FlyDSL table), sampled rows."""
+    w = W.WORKLOADS["gqa"]
+    q, k, v = W.make_qkv(w)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    assert_quant_equal(g, ref)
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=16, heads=[0, 7, 8, 15])
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, causal=True, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows, causal=True)
+    check_o(o, o_ref, rows, "gqa full")
+    check_lse(l, l_ref, rows, "gqa full")
+
+
 def test_attn_deterministic():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
@@ -372,13 +431,13 @@ def test_blockmask_to_index_exact():
         assert np.array_equal(idx[b, h, t, :n], r_idx[b, h, t, :n])
 
 
-def _sparse_case(T, H, mask, vbs, rows=None):
+def _sparse_case(T, H, mask, vbs, rows=None, Hkv=None):
     w = W.WORKLOADS["sparse"]
     S = 64 * T
-    q, k, v = W.make_qkv(w, H=H, Sq=S, Sk=S)
+    q, k, v = W.make_qkv(w, H=H, Sq=S, Sk=S, Hkv=Hkv)
     for x in (q, k, v):
         W.zero_pads(x, vbs)
-    vsc = W.v_scale(w, H=H)
+    vsc = W.v_scale(w, H=Hkv or H)
     ref = oracle.quantize_qk(q, k, vbs)
     g = gpu_quant(q, k, vbs)
     assert_quant_equal(g, ref)
