@@ -248,9 +248,6 @@ struct KeyTerms {
   uint32_t raw[2][BN];
 };
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmem = 0x020, kSgDsRead = 0x100;
-
 // At most N vector-memory operations (copies) of this wave outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
