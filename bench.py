@@ -439,6 +439,30 @@ def other_configs(dev) -> int:
     print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V, int8 QK",
                       "rows": rows, "device": info}), flush=True)
 
+    # split-K on the banded workload's 8-GPU shard: 7 heads give 224 query blocks for 256 CUs
+    w = W.WORKLOADS["band"]
+    q_np, k_np, v_np = W.make_qkv(w, H=7)
+    q, k, v = up(q_np), up(k_np), up(v_np)
+    del q_np, k_np, v_np
+    bias = up(W.bias_tensor(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]), "fp32"))
+    qk = qfa.quantize_qk(q, k)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 7, w.Sq), dtype=torch.float32, device=dev)
+    ns = qfa.splits_auto(1, 7, w.Sq, w.Sk)
+    ws = torch.empty(max(1, qfa.split_workspace_bytes(1, 7, w.Sq, w.D, ns)), dtype=torch.uint8, device=dev)
+    line = {"config": "band_shard_h7_split_k", "shape": f"B1 H7 Sq{w.Sq} Sk{w.Sk} D{w.D} bf16, fp32 bias, LSE on",
+            "auto_splits": ns}
+    fl = 4.0 * 7 * w.Sq * w.Sk * w.D
+    for n in sorted({1, 2, ns, 8}):
+        wsn = ws if n == ns else None
+        t = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=bias, out=out, lse=lse, splits=n, workspace=wsn), 10)
+        line[f"splits{n}_ms"] = round(t, 4)
+        line[f"splits{n}_frac_blend"] = round(fl / (t * 1e-3) / 1e12 / PEAK_BLEND, 4)
+    line["device"] = info
+    print(json.dumps(line), flush=True)
+    del q, k, v, bias, qk, out, lse, ws
+    torch.cuda.empty_cache()
+
     # the banded workload with the pages' bool [1,1,1,K] keep mask (raised-cosine weight > 1e-3)
     w = W.WORKLOADS["band"]
     q_np, k_np, v_np = W.make_qkv(w)

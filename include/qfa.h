@@ -58,6 +58,7 @@ extern "C" {
 #define QFA_BOOL 4 /* bytes, nonzero = true (a keep mask) */
 
 #define QFA_MAX_SEGMENTS 4
+#define QFA_MAX_SPLITS 64
 
 /* Version of this ABI (major*100 + minor). */
 int qfa_version(void);
@@ -213,6 +214,57 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
  */
 int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                       const int8_t* q8, const int8_t* k8, int32_t* s32, void* stream);
+
+/*
+ * qfa_attn_fwd_splitk — qfa_attn_fwd with each (128-row query block, head)
+ * key walk cut into num_splits contiguous ranges run by separate blocks, then
+ * combined (the split-K path and combine of ROCm/FlyDSL PR #886: "split-K
+ * combine", the LSE taken from the combined max and denominator).
+ *
+ * Split k writes its normalised partial O_k and LSE L_k (fp32) to the
+ * workspace; a combine kernel then writes, per row,
+ *   m = max_k L_k,  w_k = exp(L_k - m),  O = sum_k w_k O_k / sum_k w_k,
+ *   LSE = m + log(sum_k w_k)       (O = 0, LSE = -inf when every L_k = -inf)
+ * to out/lse with the same layouts as qfa_attn_fwd. The result equals
+ * qfa_attn_fwd's up to fp32 rounding. It fills the GPU when B*H*ceil(Sq/128)
+ * is small against the number of CUs.
+ *
+ * Arguments as qfa_attn_fwd, plus:
+ * num_splits: 1..QFA_MAX_SPLITS (1 is qfa_attn_fwd; see qfa_attn_splits_auto).
+ *           Block-sparse calls (index != NULL) take only 1
+ *           (QFA_ERR_UNSUPPORTED otherwise).
+ * workspace: device buffer of at least qfa_attn_split_workspace_bytes(B, H,
+ *           Sq, D, num_splits) bytes, 16-byte aligned, owned by the caller;
+ *           the call overwrites it and leaves nothing in it that a later
+ *           call reads (NULL allowed when num_splits == 1). Calls that run
+ *           concurrently need separate workspaces.
+ */
+int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                        const int8_t* q8, const float* qs, const float* qmu,
+                        const int8_t* k8, const float* ks,
+                        const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                        float sm_scale,
+                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                        const int32_t* index, const int32_t* count, const int32_t* vbs,
+                        const float* v_scale, int nseg, const int64_t* seg, int causal,
+                        void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                        float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qfa_attn_split_workspace_bytes — workspace qfa_attn_fwd_splitk needs:
+ * num_splits * B*H*Sq * (D + 1) * 4 bytes (0 for one split). Writes *bytes.
+ */
+int qfa_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t D, int num_splits, size_t* bytes);
+
+/*
+ * qfa_attn_splits_auto — a split count for the current device (a power of
+ * two up to 16; 1 when the unsplit grid already fills it): first enough
+ * (query block, head, split) blocks for about one round of two per CU while
+ * a split keeps at least 16 key tiles of the walk (causal calls: of the
+ * average walk), then, for long walks, more splits while each keeps at least
+ * 128 tiles, up to three rounds. Writes *num_splits.
+ */
+int qfa_attn_splits_auto(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int causal, int* num_splits);
 
 /*
  * qfa_lse_merge — exact merge of two partial softmaxes over disjoint key sets

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import QFA_BF16, QFA_BOOL, QFA_FP16, QFA_FP32, QFAError
 
 __all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
-           "quantize_workspace_bytes", "qk_scores_i32"]
+           "quantize_workspace_bytes", "qk_scores_i32", "split_workspace_bytes", "splits_auto"]
 
 _DT = {torch.bfloat16: QFA_BF16, torch.float16: QFA_FP16, torch.float32: QFA_FP32}
 
@@ -140,7 +140,7 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
              index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
              v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
              out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None, return_lse: bool = False,
-             lse: torch.Tensor | None = None):
+             lse: torch.Tensor | None = None, splits: int | str | None = None, workspace: torch.Tensor | None = None):
     """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
 
     bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
@@ -154,6 +154,9 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
     K/V may hold Hkv heads, a divisor of H (grouped-query attention; ``qk`` from
     :func:`quantize_qk` with such a K): query head h reads K/V head h // (H // Hkv), and
     ``v_scale`` is [Hkv, D].
+    splits: split-K over the key walk (dense calls): an int >= 1, or "auto" for
+        :func:`splits_auto`'s choice; the partials go to ``workspace`` (uint8 device
+        tensor of :func:`split_workspace_bytes` bytes, allocated when not given).
     """
     _no_grad(v, bias)
     q8, qs, k8, ks, qmu = qk["q8"], qk["qs"], qk["k8"], qk["ks"], qk.get("qmu")
@@ -200,12 +203,38 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
         segs = [int(x) for pair in segments for x in pair]
         nseg = len(segs) // 2
         seg = (ctypes.c_int64 * max(1, len(segs)))(*segs)
-    _lib.check(_lib.lib().qfa_attn_fwd(
-        B, H, Hkv, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
-        _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
-        bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
-        int(bool(causal)), _ptr(out), do, *ost, _ptr(lse), _stream(dev)))
+    args = (B, H, Hkv, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
+            _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
+            bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
+            int(bool(causal)), _ptr(out), do, *ost, _ptr(lse))
+    ns = 1
+    if splits == "auto":
+        ns = splits_auto(B, H, Sq, Sk, causal)
+    elif splits is not None:
+        ns = int(splits)
+    if ns == 1:
+        _lib.check(_lib.lib().qfa_attn_fwd(*args, _stream(dev)))
+    else:
+        nbytes = split_workspace_bytes(B, H, Sq, D, ns)
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _cont(workspace, "workspace", torch.uint8)
+        _lib.check(_lib.lib().qfa_attn_fwd_splitk(*args, ns, _ptr(workspace), workspace.numel(), _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def split_workspace_bytes(B: int, H: int, Sq: int, D: int, splits: int) -> int:
+    """Bytes of the split-K workspace (fp32 partial O and LSE of every split)."""
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.lib().qfa_attn_split_workspace_bytes(B, H, Sq, D, splits, ctypes.byref(n)))
+    return n.value
+
+
+def splits_auto(B: int, H: int, Sq: int, Sk: int, causal: bool = False) -> int:
+    """The library's split count for this shape on the current device (1 = no split)."""
+    n = ctypes.c_int(0)
+    _lib.check(_lib.lib().qfa_attn_splits_auto(B, H, Sq, Sk, int(bool(causal)), ctypes.byref(n)))
+    return n.value
 
 
 def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,

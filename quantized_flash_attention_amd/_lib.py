@@ -23,6 +23,9 @@ EXPORTS = (
     "qfa_quantize_qk",
     "qfa_blockmask_to_index",
     "qfa_attn_fwd",
+    "qfa_attn_fwd_splitk",
+    "qfa_attn_split_workspace_bytes",
+    "qfa_attn_splits_auto",
     "qfa_lse_merge",
     "qfa_qk_scores_i32",
 )
@@ -56,6 +59,12 @@ def _declare(L: ctypes.CDLL) -> None:
                                + [_P, _I, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
                                + [_P, _I, _I64, _I64, _I64] + [_P, _P])
     L.qfa_attn_fwd.restype = _I
+    L.qfa_attn_fwd_splitk.argtypes = L.qfa_attn_fwd.argtypes[:-1] + [_I, _P, ctypes.c_size_t, _P]
+    L.qfa_attn_fwd_splitk.restype = _I
+    L.qfa_attn_split_workspace_bytes.argtypes = [_I64] * 4 + [_I, ctypes.POINTER(ctypes.c_size_t)]
+    L.qfa_attn_split_workspace_bytes.restype = _I
+    L.qfa_attn_splits_auto.argtypes = [_I64] * 4 + [_I, ctypes.POINTER(_I)]
+    L.qfa_attn_splits_auto.restype = _I
     L.qfa_lse_merge.argtypes = ([_I64] * 4 + [_P, _I, _I64, _I64, _I64, _P] * 2
                                 + [_P, _I, _I64, _I64, _I64, _P, _P])
     L.qfa_lse_merge.restype = _I

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -163,16 +164,49 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
                     "blockmask_to_index launch");
 }
 
-int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-                 const int8_t* q8, const float* qs, const float* qmu,
-                 const int8_t* k8, const float* ks,
-                 const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
-                 float sm_scale,
-                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
-                 const int32_t* index, const int32_t* count, const int32_t* vbs,
-                 const float* v_scale, int nseg, const int64_t* seg, int causal,
-                 void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
-                 float* lse, void* stream) {
+int qfa_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t D, int num_splits, size_t* bytes) {
+  if (!bytes) return fail(QFA_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0 || H < 0 || Sq < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
+  if (D != 64 && D != 128) return fail(QFA_ERR_UNSUPPORTED, "head dimension %lld (supported: 64, 128)", (long long)D);
+  if (num_splits < 1 || num_splits > QFA_MAX_SPLITS)
+    return fail(QFA_ERR_INVALID_ARG, "num_splits %d (1..%d)", num_splits, QFA_MAX_SPLITS);
+  // fp32 partial O [splits][B*H*Sq][D], then fp32 partial LSE [splits][B*H*Sq]
+  *bytes = num_splits > 1 ? (size_t)num_splits * (size_t)(B * H * Sq) * (size_t)(D + 1) * 4u : 0;
+  return ok();
+}
+
+int qfa_attn_splits_auto(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int causal, int* num_splits) {
+  if (!num_splits) return fail(QFA_ERR_INVALID_ARG, "num_splits is NULL");
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
+  int ncu = 0;
+  int st;
+  if ((st = hip_status(qfa::device_cu_count(&ncu), "device query"))) return st;
+  // Powers of two only (odd counts measured slower). First fill about one
+  // round of two blocks per CU while a split keeps >= 16 key tiles of the
+  // (causal: average) walk; then, for long walks, keep halving them while a
+  // split keeps >= 128 tiles, up to three rounds, so the last round's tail is
+  // short. Tuned on banded B1 H1..14 Sq1024..4096 Sk4096..33600 shapes.
+  const int64_t blocks = (Sq + 127) / 128 * B * H;
+  const int64_t walk = causal ? ((Sk + 63) / 64 + 1) / 2 : (Sk + 63) / 64;
+  const int64_t slots = 2 * (int64_t)std::max(ncu, 1);
+  int64_t n = 1;
+  while (n < 16 && blocks * n * 100 < 85 * slots && walk / (2 * n) >= 8) n *= 2;
+  while (n < 16 && blocks * n < 3 * slots && walk / n >= 128) n *= 2;
+  *num_splits = (int)n;
+  return ok();
+}
+
+namespace {
+int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                  const int8_t* q8, const float* qs, const float* qmu,
+                  const int8_t* k8, const float* ks,
+                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                  float sm_scale,
+                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                  const int32_t* index, const int32_t* count, const int32_t* vbs,
+                  const float* v_scale, int nseg, const int64_t* seg, int causal,
+                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                  float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   int st;
   if ((st = check_dims(B, H, Sq, Sk, D))) return st;
   if ((st = check_kv_heads(H, Hkv))) return st;
@@ -211,10 +245,20 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
     if (index) return fail(QFA_ERR_UNSUPPORTED, "causal attention with a block-sparse mask");
     if (nseg != 0) return fail(QFA_ERR_UNSUPPORTED, "causal attention with key segments");
   }
-  // one 128-row block per (query tile, head), heads padded to 8 for causal calls;
-  // 256 threads per block keep the launch within 2^32 threads
-  if ((Sq + 127) / 128 * ((B * H + 7) / 8 * 8) > (1ll << 24))
+  if (num_splits < 1 || num_splits > QFA_MAX_SPLITS)
+    return fail(QFA_ERR_INVALID_ARG, "num_splits %d (1..%d)", num_splits, QFA_MAX_SPLITS);
+  if (num_splits > 1 && index) return fail(QFA_ERR_UNSUPPORTED, "split-K with a block-sparse mask");
+  // one 128-row block per (query tile, head, split), padded to 8 units for
+  // causal calls; 256 threads per block keep the launch within 2^32 threads
+  if ((Sq + 127) / 128 * ((B * H * num_splits + 7) / 8 * 8) > (1ll << 24))
     return fail(QFA_ERR_UNSUPPORTED, "more than 2^24 blocks of 128 query rows");
+  if (num_splits > 1) {
+    size_t need = 0;
+    qfa_attn_split_workspace_bytes(B, H, Sq, D, num_splits, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+      return fail(QFA_ERR_INVALID_ARG, "split workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+  }
   if (nseg < 0 || nseg > QFA_MAX_SEGMENTS) return fail(QFA_ERR_INVALID_ARG, "nseg %d (0..4)", nseg);
   if (nseg > 0 && !seg) return fail(QFA_ERR_INVALID_ARG, "seg is NULL with nseg > 0");
   int64_t prev_end = 0;
@@ -243,7 +287,43 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
   a.v_scale = v_scale;
   a.out = out; a.out_dtype = out_dtype; a.o_sb = o_sb; a.o_sh = o_sh; a.o_ss = o_ss;
   a.lse = lse;
+  a.nsplit = num_splits;
+  if (num_splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = a.part_o + (size_t)num_splits * (size_t)(B * H * Sq) * (size_t)D;
+  }
   return hip_status(qfa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+}
+}  // namespace
+
+int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                 const int8_t* q8, const float* qs, const float* qmu,
+                 const int8_t* k8, const float* ks,
+                 const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                 float sm_scale,
+                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                 const int32_t* index, const int32_t* count, const int32_t* vbs,
+                 const float* v_scale, int nseg, const int64_t* seg, int causal,
+                 void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                 float* lse, void* stream) {
+  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, q8, qs, qmu, k8, ks, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
+                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       out, out_dtype, o_sb, o_sh, o_ss, lse, 1, nullptr, 0, stream);
+}
+
+int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                        const int8_t* q8, const float* qs, const float* qmu,
+                        const int8_t* k8, const float* ks,
+                        const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                        float sm_scale,
+                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                        const int32_t* index, const int32_t* count, const int32_t* vbs,
+                        const float* v_scale, int nseg, const int64_t* seg, int causal,
+                        void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                        float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, q8, qs, qmu, k8, ks, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
+                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
 }
 
 int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,

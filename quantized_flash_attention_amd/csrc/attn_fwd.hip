@@ -362,16 +362,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[NSTG][V_BYTES];
   __shared__ __attribute__((aligned(16))) KeyTerms kt[NSTG];
 
-  int bh, qt;
+  // work unit = (head, split); a split-K call cuts each walk into ns ranges
+  const int ns = (SPARSE || DUMP) ? 1 : a.nsplit;
+  int bh, qt, split;
   if constexpr (CAUSAL) {
     const int L = causal_order((int)blockIdx.x, total_blocks, a.ncu);
-    const int bh8 = total_blocks / qtiles;
-    bh = L % bh8;
-    qt = qtiles - 1 - L / bh8;
-    if (bh >= a.B * a.H) return;   // head padding: the whole block leaves before any barrier
+    const int u8 = total_blocks / qtiles;
+    const int unit = L % u8;
+    qt = qtiles - 1 - L / u8;
+    if (unit >= a.B * a.H * ns) return;   // unit padding: the whole block leaves before any barrier
+    bh = unit / ns;
+    split = unit % ns;
   } else {
     const int bid = xcd_remap((int)blockIdx.x, total_blocks);
-    bh = bid / qtiles;
+    const int unit = bid / qtiles;
+    bh = unit / ns;
+    split = unit % ns;
     qt = bid % qtiles;
   }
   const int b = bh / a.H, h = bh % a.H;
@@ -392,6 +398,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const __attribute__((address_space(4))) int32_t* list_a = nullptr;
   const __attribute__((address_space(4))) int32_t* list_b = nullptr;
   int ntk = 0, n_tiles, na = 0, nb = 0, ia = 0, ib = 0;
+  int it0 = 0;   // walk position of this block's first tile (split-K: its range start)
   if constexpr (SPARSE) {
     ntk = a.Sk / BN;
     const int qa = 2 * qt, qb = 2 * qt + 1;
@@ -404,6 +411,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   } else {
     n_tiles = a.seg_ntiles;
     if constexpr (CAUSAL) n_tiles = min(n_tiles, (min(a.Sk, qt * BM + BM) + BN - 1) / BN);
+    // split-K: walk positions [it0, n_tiles) of the whole walk (ns * walk < 2^31)
+    it0 = split * n_tiles / ns;
+    n_tiles = (split + 1) * n_tiles / ns;
   }
   const __attribute__((address_space(4))) int32_t* vbs = (const __attribute__((address_space(4))) int32_t*)a.vbs;
   // The key tiles of this block in loop order, one per call: the tile, the
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // the two ascending lists (entries are clamped into [0, ntk); lists that
   // are not strictly ascending give unspecified results but stay in bounds,
   // and the walk ends after at most na + nb steps). Wave-uniform throughout.
-  int cur_it = -1, cur_tile = -1, cur_slo = 0, cur_shi = 0;
+  int cur_it = it0 - 1, cur_tile = -1, cur_slo = 0, cur_shi = 0;
   auto next_tile = [&](int& tile, int& lo, int& hi, int& valid) __attribute__((always_inline)) {
     ++cur_it;
     if constexpr (SPARSE) {
@@ -615,7 +625,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 
     if constexpr (DUMP) {
       // S(iter) out (int32 [B,H,Sq,Sk]), S(iter+1) MFMAs, K copy, barrier;
-      // the walk of a score dump is the single segment [0, Sk)
+      // the walk of a score dump is the single segment [0, Sk), unsplit
       const int tile = iter, lo = iter * BN, hi = min(a.Sk, lo + BN);
       int32_t* srow = (int32_t*)a.out + qrow * a.Sk;
 #pragma unroll
@@ -666,11 +676,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     }
     copy_v(st2, t2, v2);                        // V(iter+2) over V(iter-1)
     if (CAUSAL && diag) {
-      // the walk is the single segment [0, Sk), so tile `iter` holds keys
-      // iter*BN + [0, BN); only waves whose first row lies before the tile's
-      // last key see a key past their row
-      if (qt * BM + wave * 32 < iter * BN + BN - 1) {
-        const int lim = q - iter * BN;   // last attended key of this row, tile-relative
+      // the walk is the single segment [0, Sk), so tile it0 + iter holds keys
+      // (it0 + iter)*BN + [0, BN); only waves whose first row lies before the
+      // tile's last key see a key past their row
+      const int key0 = (it0 + iter) * BN;
+      if (qt * BM + wave * 32 < key0 + BN - 1) {
+        const int lim = q - key0;   // last attended key of this row, tile-relative
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -768,10 +779,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // copy with the mask, so the main loop carries none of its code. Other
   // instances test n_tiles itself on every pass: a block-sparse walk sets
   // it (from INT32_MAX) only when its lists run out.
-  const int n_plain = CAUSAL ? min(n_tiles, (qt * BM + 1) / BN) : 0;
+  // (loop counts are relative to it0; n_tiles is a walk position)
+  const int n_plain = CAUSAL ? max(0, min(n_tiles, (qt * BM + 1) / BN) - it0) : 0;
   int st0 = 0, st1 = 1, st2 = 2;
   int iter = 0;
-  for (; iter < (CAUSAL ? n_plain : n_tiles); ++iter) {
+  for (; iter < (CAUSAL ? n_plain : n_tiles - it0); ++iter) {
     tile_body(iter, st0, st1, st2, false);
     const int tmp = st0;
     st0 = st1;
@@ -779,7 +791,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     st2 = tmp;
   }
   if constexpr (CAUSAL) {
-    for (; iter < n_tiles; ++iter) {
+    for (; iter < n_tiles - it0; ++iter) {
       tile_body(iter, st0, st1, st2, true);
       const int tmp = st0;
       st0 = st1;
@@ -790,7 +802,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // drain this wave's remaining copies (they target stages nobody reads)
   wait_vmcnt<0>();
 
-  if constexpr (!DUMP) store_rows<D, LSE>(a, o, lsum, m_run, b, h, hk, q, qrow, qvalid, hl);
+  if constexpr (!DUMP) {
+    if (LSE && ns > 1) {
+      // split-K partial: normalised fp32 O and its LSE into this split's slice
+      const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+      AttnArgs p = a;
+      p.out = a.part_o + split * rows * D;
+      p.out_dtype = FP32;
+      p.o_sb = (int64_t)a.H * a.Sq * D;
+      p.o_sh = (int64_t)a.Sq * D;
+      p.o_ss = D;
+      p.lse = a.part_lse + split * rows;
+      store_rows<D, LSE>(p, o, lsum, m_run, b, h, hk, q, qrow, qvalid, hl);
+    } else {
+      store_rows<D, LSE>(a, o, lsum, m_run, b, h, hk, q, qrow, qvalid, hl);
+    }
+  }
 }
 
 
@@ -798,30 +825,36 @@ template <int D, int VT>
 hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   const bool sparse = a.index != nullptr;
   const int qtiles = (a.Sq + 127) / 128;   // 128 query rows (two 64-query tiles) per block
-  const int total = qtiles * a.B * a.H;
+  const int ns = sparse ? 1 : a.nsplit;    // split-K ranges per walk (dense calls)
+  const int total = qtiles * a.B * a.H * ns;
   if (total == 0) return hipSuccess;
+  // split partials always carry their LSE
+  const bool lse = a.lse != nullptr || ns > 1;
   if (sparse) {
-    if (a.lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, true, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
   } else if (a.causal) {
     // a keep mask (bool bias) runs in the unbiased instance; the grid pads
-    // B*H to a multiple of 8 (see causal_order)
-    const int total8 = qtiles * ((a.B * a.H + 7) / 8 * 8);
+    // the (head, split) units to a multiple of 8 (see causal_order)
+    const int total8 = qtiles * ((a.B * a.H * ns + 7) / 8 * 8);
     if (a.bias && a.bias_dtype != BOOL) {
-      if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, false, true, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
       else attn_fwd_kernel<D, VT, 4, false, true, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
     } else {
-      if (a.lse) attn_fwd_kernel<D, VT, 4, false, false, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, false, false, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
       else attn_fwd_kernel<D, VT, 4, false, false, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
     }
   } else if (a.bias && a.bias_dtype != BOOL) {
-    if (a.lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);
   } else {
-    if (a.lse) attn_fwd_kernel<D, VT, 4, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, false, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  CombineArgs c{a.B, a.H, a.Sq, D, ns, a.part_o, a.part_lse, a.out, a.out_dtype, a.o_sb, a.o_sh, a.o_ss, a.lse};
+  return launch_split_combine(c, s);
 }
 
 template <int D>
@@ -847,6 +880,22 @@ void derive_segments(AttnArgs& a) {
 
 }  // namespace
 
+hipError_t device_cu_count(int* ncu) {
+  // queried once per device
+  static std::atomic<int> ncu_of[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int n = dev >= 0 && dev < 64 ? ncu_of[dev].load(std::memory_order_relaxed) : 0;
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) ncu_of[dev].store(n, std::memory_order_relaxed);
+  }
+  *ncu = n;
+  return hipSuccess;
+}
+
 hipError_t launch_qk_scores(const AttnArgs& args, hipStream_t s) {
   AttnArgs a = args;
   derive_segments(a);
@@ -856,19 +905,10 @@ hipError_t launch_qk_scores(const AttnArgs& args, hipStream_t s) {
 hipError_t launch_attn_fwd(const AttnArgs& args, hipStream_t s) {
   AttnArgs a = args;
   derive_segments(a);
+  if (a.nsplit < 1 || a.index) a.nsplit = 1;
   if (a.causal) {
-    // compute units of the current device, queried once per device
-    static std::atomic<int> ncu_of[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    const hipError_t e = device_cu_count(&a.ncu);
     if (e != hipSuccess) return e;
-    int ncu = dev >= 0 && dev < 64 ? ncu_of[dev].load(std::memory_order_relaxed) : 0;
-    if (ncu == 0) {
-      e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-      if (dev >= 0 && dev < 64) ncu_of[dev].store(ncu, std::memory_order_relaxed);
-    }
-    a.ncu = ncu;
   }
   if (a.D == 128) return a.v_dtype == BF16 ? launch_d_vt<128, BF16>(a, s) : launch_d_vt<128, FP16>(a, s);
   return a.v_dtype == BF16 ? launch_d_vt<64, BF16>(a, s) : launch_d_vt<64, FP16>(a, s);

@@ -62,7 +62,54 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   if (a.l && cg == 0) a.l[r] = L;
 }
 
+// n partials of one row: m = max_k L_k; w_k = exp(L_k - m); O = sum_k w_k O_k
+// / sum_k w_k; L = m + log(sum_k w_k) (FlyDSL PR #886: the split-K combine
+// from the combined max and denominator). Empty partials (L_k = -inf) weigh
+// 0 and are not read; a row empty in every split gives O = 0, L = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void split_combine_kernel(CombineArgs a) {
+  constexpr int G = D / 8;
+  constexpr int RPB = 256 / G;
+  const int cg = threadIdx.x % G;
+  const int64_t rows = a.B * a.H * a.S;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / G;
+  if (r >= rows) return;
+  const int64_t bh = r / a.S, s = r % a.S, b = bh / a.H, h = bh % a.H;
+  float m = -INFINITY;
+  for (int k = 0; k < a.nsplit; ++k) m = fmaxf(m, a.pl[k * rows + r]);
+  float out[8];
+  for (int i = 0; i < 8; ++i) out[i] = 0.0f;
+  float L = -INFINITY;
+  if (m != -INFINITY) {
+    float wsum = 0.0f;
+    for (int k = 0; k < a.nsplit; ++k) {
+      const float lk = a.pl[k * rows + r];
+      if (lk == -INFINITY) continue;
+      const float w = expf(lk - m);
+      wsum += w;
+      float f[8];
+      load8(a.po, FP32, (k * rows + r) * D + cg * 8, f);
+      for (int i = 0; i < 8; ++i) out[i] += w * f[i];
+    }
+    const float inv = 1.0f / wsum;
+    for (int i = 0; i < 8; ++i) out[i] *= inv;
+    L = m + logf(wsum);
+  }
+  store8(a.o, a.o_dtype, b * a.o_sb + h * a.o_sh + s * a.o_ss + cg * 8, out);
+  if (a.l && cg == 0) a.l[r] = L;
+}
+
 }  // namespace
+
+hipError_t launch_split_combine(const CombineArgs& a, hipStream_t s) {
+  const int64_t rows = a.B * a.H * a.S;
+  if (rows == 0) return hipSuccess;
+  const int rpb = 256 / (int)(a.D / 8);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (a.D == 128) split_combine_kernel<128><<<grid, 256, 0, s>>>(a);
+  else split_combine_kernel<64><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t rows = a.B * a.H * a.S;

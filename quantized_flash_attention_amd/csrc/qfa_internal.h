@@ -68,6 +68,13 @@ struct AttnArgs {
   int seg_lo[4], seg_hi[4];
   int causal;           // self-attention with key j > row i excluded (Sq == Sk, one segment [0, Sk))
   int ncu;              // compute units of the device (block order of causal calls)
+  // split-K: each (query block, head) walk is cut into nsplit contiguous
+  // ranges, one block each; with nsplit > 1 a block writes its normalised
+  // fp32 partial O to part_o [nsplit][B*H*Sq][D] and its LSE to part_lse
+  // [nsplit][B*H*Sq] instead of out/lse (dense calls only)
+  int nsplit;
+  float* part_o;
+  float* part_lse;
   // derived by the launcher from the segments: first key tile of segment g,
   // number of tiles before segment g (INT32_MAX for absent segments), and
   // the total number of key tiles of the call
@@ -79,6 +86,8 @@ struct AttnArgs {
   float* lse;           // nullable
 };
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t s);
+// compute units of the current device (cached per device)
+hipError_t device_cu_count(int* ncu);
 // int32 scores of the attention kernel's QK stage into a.out (int32 [B,H,Sq,Sk]);
 // uses q8, k8, sizes and one segment [0, Sk).
 hipError_t launch_qk_scores(const AttnArgs& a, hipStream_t s);
@@ -90,6 +99,16 @@ struct MergeArgs {
   void* o; int o_dtype; int64_t o_sb, o_sh, o_ss; float* l;
 };
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+
+// n-way combine of split partials by their LSE into O (+ LSE)
+struct CombineArgs {
+  int64_t B, H, S, D;
+  int nsplit;
+  const float* po;      // [nsplit][B*H*S][D] fp32, normalised partial outputs
+  const float* pl;      // [nsplit][B*H*S] fp32 partial LSEs (-inf: nothing attended)
+  void* o; int o_dtype; int64_t o_sb, o_sh, o_ss; float* l;   // l nullable
+};
+hipError_t launch_split_combine(const CombineArgs& a, hipStream_t s);
 
 // ---- device helpers ----------------------------------------------------------
 

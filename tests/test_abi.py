@@ -75,6 +75,38 @@ def _attn(**kw):
                                    *a["o_s"], a["lse"], None)
 
 
+def _attn_split(ns, ws=FAKE, wsb=1 << 30, **kw):
+    a = dict(B=1, H=2, Sq=128, Sk=128, D=128, qk=[FAKE] * 5, v=FAKE, vdt=1, v_s=(32768, 16384, 128), scale=0.088,
+             bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None, causal=0,
+             out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
+    a.update(kw)
+    return _lib.lib().qfa_attn_fwd_splitk(a["B"], a["H"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"],
+                                          a["vdt"], *a["v_s"], ctypes.c_float(a["scale"]), a["bias"], a["bdt"],
+                                          *a["b_s"], a["index"], a["count"], a["vbs"], a["vsc"], a["nseg"],
+                                          a["seg"], a["causal"], a["out"], a["odt"], *a["o_s"], a["lse"], ns, ws,
+                                          wsb, None)
+
+
+def test_split_rejects_bad_arguments():
+    L = _lib.lib()
+    n = ctypes.c_size_t(0)
+    assert L.qfa_attn_split_workspace_bytes(2, 3, 100, 128, 4, ctypes.byref(n)) == _lib.QFA_OK
+    assert n.value == 4 * 2 * 3 * 100 * 129 * 4
+    assert L.qfa_attn_split_workspace_bytes(2, 3, 100, 64, 1, ctypes.byref(n)) == _lib.QFA_OK and n.value == 0
+    assert L.qfa_attn_split_workspace_bytes(2, 3, 100, 64, 0, ctypes.byref(n)) == _lib.QFA_ERR_INVALID_ARG
+    assert L.qfa_attn_split_workspace_bytes(2, 3, 100, 96, 2, ctypes.byref(n)) == _lib.QFA_ERR_UNSUPPORTED
+    for ns in (0, -1, 65):
+        assert _attn_split(ns) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn_split(4, index=FAKE, count=FAKE) == _lib.QFA_ERR_UNSUPPORTED
+    assert b"block-sparse" in L.qfa_last_error()
+    need = 4 * 2 * 128 * 129 * 4
+    assert _attn_split(4, wsb=need - 1) == _lib.QFA_ERR_INVALID_ARG
+    assert b"workspace" in L.qfa_last_error()
+    assert _attn_split(4, ws=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn_split(4, ws=ctypes.c_void_p(0x10008)) == _lib.QFA_ERR_INVALID_ARG   # misaligned
+    assert _attn_split(4, D=80) == _lib.QFA_ERR_UNSUPPORTED   # the plain checks still apply
+
+
 def _segs(*pairs):
     flat = [x for p in pairs for x in p]
     return (ctypes.c_int64 * len(flat))(*flat)

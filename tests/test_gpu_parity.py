@@ -368,6 +368,73 @@ def test_gqa_full_size_sampled():
     check_lse(l, l_ref, rows, "gqa full")
 
 
+SPLIT_CASES = {
+    # (workload, shape, splits, options); ranges of the split walks are ragged, and some
+    # splits get no tile at all (causal short walks, more splits than tiles)
+    "dense_ragged_2": ("dense4k", dict(H=2, Sq=333, Sk=1000), 2, {}),
+    "dense_ragged_7": ("dense4k", dict(H=2, Sq=333, Sk=1000), 7, {}),
+    "band_bias_segments_3": ("band", dict(H=2, Sq=200, Sk=2100), 3,
+                             {"bias": True, "segments": [(3, 600), (700, 1), (1500, 599)]}),
+    "causal_4": ("dense4k", dict(H=2, Sq=517, Sk=517), 4, {"causal": True}),
+    "gqa_keep_mask_5": ("band", dict(H=4, Hkv=2, Sq=256, Sk=1680), 5, {"keep": True}),
+    "d64_fp16_vscale_fp32out_3": ("d64", dict(B=2, H=2, Sq=300, Sk=517), 3, {"vscale": True, "fp32out": True}),
+    "more_splits_than_tiles": ("tiny", dict(Sq=100, Sk=130), 8, {}),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_split_k_parity(case):
+    """Split-K (partials + n-way combine) against the oracle's unsplit attention, with and
+    without the LSE, and against the unsplit GPU call."""
+    wn, shape, ns, opt = SPLIT_CASES[case]
+    w = W.WORKLOADS[wn]
+    q, k, v = W.make_qkv(w, **shape)
+    H, Hkv, Sk = q.shape[1], k.shape[1], k.shape[2]
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    bias_ref = bias_gpu = None
+    if opt.get("bias"):
+        bias_ref = W.bias_tensor(W.band_bias(Sk, core=(Sk // 5, Sk - 2 * (Sk // 5)), skirt=Sk // 5), "fp32")
+        bias_gpu = up(bias_ref)
+    if opt.get("keep"):
+        keep = np.exp(W.band_bias(Sk, core=(Sk // 5, Sk - 2 * (Sk // 5)), skirt=Sk // 5)) > 1e-3
+        keep = keep.reshape(1, 1, 1, Sk)
+        bias_ref = np.where(keep, 0.0, -np.inf).astype(np.float32)
+        bias_gpu = torch.from_numpy(keep).to(DEV)
+    vsc = W.v_scale(w, H=Hkv) if opt.get("vscale") else None
+    seg, causal = opt.get("segments"), opt.get("causal", False)
+    out_dtype = torch.float32 if opt.get("fp32out") else None
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias_ref, v_scale=vsc, segments=seg, causal=causal)
+    kw = dict(bias=bias_gpu, v_scale=None if vsc is None else up(vsc), segments=seg, causal=causal,
+              out_dtype=out_dtype)
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, splits=ns, **kw)
+    check_o(o, o_ref, what=case)
+    check_lse(l, l_ref, what=case)
+    o2 = qfa.attn_fwd(g, up(v), w.sm_scale, splits=ns, **kw)
+    check_o(o2, o_ref, what=case + " no LSE")
+    o1, l1 = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, **kw)
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(l)) and (l[fin] - l1[fin]).abs().max().item() <= 1e-3
+
+
+def test_split_k_band_shard_sampled():
+    """The banded workload's per-GPU shard with 7 heads (B1 H7 Sq4096 Sk33600, 224 query
+    blocks for 256 CUs) with the library's own split count, on sampled rows."""
+    w = W.WORKLOADS["band"]
+    q, k, v = W.make_qkv(w, H=7)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    ns = qfa.splits_auto(1, 7, w.Sq, w.Sk)
+    assert ns > 1
+    bias = W.bias_tensor(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]), "fp32")
+    rows = sample_rows(w.B, 7, w.Sq, per_head=24, heads=[0, 6])
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, bias=up(bias), return_lse=True, splits="auto")
+    check_o(o, o_ref, rows, f"band shard, {ns} splits")
+    check_lse(l, l_ref, rows, f"band shard, {ns} splits")
+
+
 def test_attn_deterministic():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
