@@ -272,7 +272,7 @@ def main() -> int:
 
 
 COPY_BYTES = 256 << 20
-UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false, false, false>"
+UNMASKED_KERNEL = "attn_fwd_kernel<128, 1, 4, false, false, false, false, false, false>"
 
 
 def _counter_per_dispatch(path: str, counter: str):
@@ -429,14 +429,17 @@ def other_configs(dev) -> int:
         scale = D ** -0.5
         t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
         t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, scale, causal=True, out=out, lse=lse), 20)
+        t_b = _time_ms(lambda: qfa.attn_fwd_unquant(q, k, v, scale, causal=True, out=out, lse=lse), 20)
         fl = 4.0 * B * H * S * S * D / 2
         rows.append({"shape": f"B{B} S{S} H{H} Hkv{Hkv} D{D}", "quantize_us": round(t_q * 1e3, 1),
                      "attn_us": round(t_a * 1e3, 1), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
                      "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
-                     "end_to_end_us": round((t_q + t_a) * 1e3, 1), "page_flydsl_lse_us": page_us})
+                     "end_to_end_us": round((t_q + t_a) * 1e3, 1),
+                     "bf16qk_us": round(t_b * 1e3, 1), "bf16qk_tflops": round(fl / (t_b * 1e-3) / 1e12, 1),
+                     "page_flydsl_lse_us": page_us})
         del q, k, v, ws, qk, out, lse
     torch.cuda.empty_cache()
-    print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V, int8 QK",
+    print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V; int8 QK, and bf16 QK (bf16qk_*)",
                       "rows": rows, "device": info}), flush=True)
 
     # split-K on the banded workload's 8-GPU shard: 7 heads give 224 query blocks for 256 CUs

@@ -251,6 +251,34 @@ int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qfa_attn_fwd_unquant — the same attention with Q K^T on the unquantized
+ * bf16/fp16 Q and K (the BF16-QK ablation of FastVideo
+ * "minimax_h3_sparse_int8": sparse_sm89_attention with int8_qk=False runs
+ * the same kernel on the unquantized, uncentred Q and K).
+ *
+ *   s_ij = sm_scale * (q_i . k_j) + bias_j, products exact, accumulated in
+ *   fp32 by the bf16/fp16 MFMA; softmax, PV, masks, LSE, GQA, causal and
+ *   split-K as qfa_attn_fwd_splitk (the LSE needs no centring term).
+ *
+ * q:        [B,H,Sq,D] of dtype, strides (q_sb, q_sh, q_ss) in elements.
+ * k:        [B,Hkv,Sk,D] of dtype, strides (k_sb, k_sh, k_ss); k_ss below
+ *           2^24 (else QFA_ERR_UNSUPPORTED).
+ * v:        [B,Hkv,Sk,D] of dtype (QFA_BF16 or QFA_FP16: one type for Q, K
+ *           and V). Base pointers and row strides 16-byte aligned.
+ * Every other argument as qfa_attn_fwd_splitk (num_splits 1 for none).
+ */
+int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                         const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                         const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                         const void* v, int dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                         float sm_scale,
+                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                         const int32_t* index, const int32_t* count, const int32_t* vbs,
+                         const float* v_scale, int nseg, const int64_t* seg, int causal,
+                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * qfa_attn_split_workspace_bytes — workspace qfa_attn_fwd_splitk needs:
  * num_splits * B*H*Sq * (D + 1) * 4 bytes (0 for one split). Writes *bytes.
  */

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import QFA_BF16, QFA_BOOL, QFA_FP16, QFA_FP32, QFAError
 
 __all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
-           "quantize_workspace_bytes", "qk_scores_i32", "split_workspace_bytes", "splits_auto"]
+           "quantize_workspace_bytes", "qk_scores_i32", "split_workspace_bytes", "splits_auto", "attn_fwd_unquant"]
 
 _DT = {torch.bfloat16: QFA_BF16, torch.float16: QFA_FP16, torch.float32: QFA_FP32}
 
@@ -136,42 +136,16 @@ def _shape(t, name, shape):
         raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
 
 
-def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,
-             index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
-             v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
-             out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None, return_lse: bool = False,
-             lse: torch.Tensor | None = None, splits: int | str | None = None, workspace: torch.Tensor | None = None):
-    """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
-
-    bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
-        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16. A bool
-        tensor of that layout is a keep mask (True attends), applied through
-        the key terms at no per-score cost.
-    index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
-    segments: up to 4 ascending disjoint (start, length) key ranges.
-    causal: self-attention (Sq == Sk) where row i attends keys j <= i only.
-    return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
-    K/V may hold Hkv heads, a divisor of H (grouped-query attention; ``qk`` from
-    :func:`quantize_qk` with such a K): query head h reads K/V head h // (H // Hkv), and
-    ``v_scale`` is [Hkv, D].
-    splits: split-K over the key walk (dense calls): an int >= 1, or "auto" for
-        :func:`splits_auto`'s choice; the partials go to ``workspace`` (uint8 device
-        tensor of :func:`split_workspace_bytes` bytes, allocated when not given).
-    """
+def _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, unquant, v, sm_scale, bias, index, count, vbs, v_scale, segments,
+               causal, out, out_dtype, return_lse, lse, splits, workspace):
+    """Shared marshalling of the attention entry points: everything but the Q/K operands."""
     _no_grad(v, bias)
-    q8, qs, k8, ks, qmu = qk["q8"], qk["qs"], qk["k8"], qk["ks"], qk.get("qmu")
-    B, H, Sq, D = q8.shape
-    Hkv, Sk = k8.shape[1], k8.shape[2]
     if v.shape != (B, Hkv, Sk, D):
         raise ValueError(f"v shape {tuple(v.shape)} != {(B, Hkv, Sk, D)}")
-    _shape(k8, "k8", (B, Hkv, Sk, D)), _shape(qs, "qs", (B, H, Sq)), _shape(ks, "ks", (B, Hkv, Sk))
-    _shape(qmu, "qmu", (B, H, Sq)), _shape(v_scale, "v_scale", (Hkv, D))
-    _shape(out, "out", (B, H, Sq, D)), _shape(lse, "lse", (B, H, Sq))
+    _shape(v_scale, "v_scale", (Hkv, D)), _shape(out, "out", (B, H, Sq, D)), _shape(lse, "lse", (B, H, Sq))
     if index is not None:
         T = Sk // 64
         _shape(index, "index", (B, H, T, T)), _shape(count, "count", (B, H, T)), _shape(vbs, "vbs", (T,))
-    _cont(q8, "q8", torch.int8), _cont(k8, "k8", torch.int8)
-    _cont(qs, "qs", torch.float32), _cont(ks, "ks", torch.float32), _cont(qmu, "qmu", torch.float32)
     dv, *vst = _view(v, "v")
     dev = v.device
     if sm_scale is None:
@@ -203,24 +177,84 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
         segs = [int(x) for pair in segments for x in pair]
         nseg = len(segs) // 2
         seg = (ctypes.c_int64 * max(1, len(segs)))(*segs)
-    args = (B, H, Hkv, Sq, Sk, D, _ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks),
-            _ptr(v), dv, *vst, ctypes.c_float(sm_scale),
-            bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale), nseg, seg,
-            int(bool(causal)), _ptr(out), do, *ost, _ptr(lse))
+    masks = (ctypes.c_float(sm_scale), bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale),
+             nseg, seg, int(bool(causal)), _ptr(out), do, *ost, _ptr(lse))
     ns = 1
     if splits == "auto":
         ns = splits_auto(B, H, Sq, Sk, causal)
     elif splits is not None:
         ns = int(splits)
-    if ns == 1:
-        _lib.check(_lib.lib().qfa_attn_fwd(*args, _stream(dev)))
+    nbytes = split_workspace_bytes(B, H, Sq, D, ns) if ns > 1 else 0
+    if nbytes and workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _cont(workspace, "workspace", torch.uint8)
+    wsp, wsn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    L = _lib.lib()
+    if unquant:
+        _lib.check(L.qfa_attn_fwd_unquant(B, H, Hkv, Sq, Sk, D, *qk_args, _ptr(v), dv, *vst, *masks, ns, wsp, wsn,
+                                          _stream(dev)))
+    elif ns == 1:
+        _lib.check(L.qfa_attn_fwd(B, H, Hkv, Sq, Sk, D, *qk_args, _ptr(v), dv, *vst, *masks, _stream(dev)))
     else:
-        nbytes = split_workspace_bytes(B, H, Sq, D, ns)
-        if workspace is None:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        _cont(workspace, "workspace", torch.uint8)
-        _lib.check(_lib.lib().qfa_attn_fwd_splitk(*args, ns, _ptr(workspace), workspace.numel(), _stream(dev)))
+        _lib.check(L.qfa_attn_fwd_splitk(B, H, Hkv, Sq, Sk, D, *qk_args, _ptr(v), dv, *vst, *masks, ns, wsp, wsn,
+                                         _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: torch.Tensor | None = None,
+             index: torch.Tensor | None = None, count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
+             v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
+             out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None, return_lse: bool = False,
+             lse: torch.Tensor | None = None, splits: int | str | None = None, workspace: torch.Tensor | None = None):
+    """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
+
+    bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
+        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16. A bool
+        tensor of that layout is a keep mask (True attends), applied through
+        the key terms at no per-score cost.
+    index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
+    segments: up to 4 ascending disjoint (start, length) key ranges.
+    causal: self-attention (Sq == Sk) where row i attends keys j <= i only.
+    return_lse / lse: write the fp32 [B,H,Sq] natural-log LSE (into ``lse`` if given).
+    K/V may hold Hkv heads, a divisor of H (grouped-query attention; ``qk`` from
+    :func:`quantize_qk` with such a K): query head h reads K/V head h // (H // Hkv), and
+    ``v_scale`` is [Hkv, D].
+    splits: split-K over the key walk (dense calls): an int >= 1, or "auto" for
+        :func:`splits_auto`'s choice; the partials go to ``workspace`` (uint8 device
+        tensor of :func:`split_workspace_bytes` bytes, allocated when not given).
+    """
+    q8, qs, k8, ks, qmu = qk["q8"], qk["qs"], qk["k8"], qk["ks"], qk.get("qmu")
+    B, H, Sq, D = q8.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    _shape(k8, "k8", (B, Hkv, Sk, D)), _shape(qs, "qs", (B, H, Sq)), _shape(ks, "ks", (B, Hkv, Sk))
+    _shape(qmu, "qmu", (B, H, Sq))
+    _cont(q8, "q8", torch.int8), _cont(k8, "k8", torch.int8)
+    _cont(qs, "qs", torch.float32), _cont(ks, "ks", torch.float32), _cont(qmu, "qmu", torch.float32)
+    qk_args = (_ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks))
+    return _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, False, v, sm_scale, bias, index, count, vbs, v_scale, segments,
+                      causal, out, out_dtype, return_lse, lse, splits, workspace)
+
+
+def attn_fwd_unquant(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sm_scale: float | None = None, *,
+                     bias: torch.Tensor | None = None, index: torch.Tensor | None = None,
+                     count: torch.Tensor | None = None, vbs: torch.Tensor | None = None,
+                     v_scale: torch.Tensor | None = None, segments=None, causal: bool = False,
+                     out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+                     return_lse: bool = False, lse: torch.Tensor | None = None, splits: int | str | None = None,
+                     workspace: torch.Tensor | None = None):
+    """The BF16-QK ablation: the same attention with Q K^T on the unquantized, uncentred
+    bf16/fp16 Q [B,H,Sq,D] and K [B,Hkv,Sk,D] (strided views allowed; Q, K and V of one
+    dtype). Every other argument as :func:`attn_fwd`."""
+    _no_grad(q, k)
+    B, H, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Sk, D) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must agree in B, D and dtype")
+    _, *qst = _view(q, "q")
+    _, *kst = _view(k, "k")
+    qk_args = (_ptr(q), *qst, _ptr(k), *kst)
+    return _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, True, v, sm_scale, bias, index, count, vbs, v_scale, segments,
+                      causal, out, out_dtype, return_lse, lse, splits, workspace)
 
 
 def split_workspace_bytes(B: int, H: int, Sq: int, D: int, splits: int) -> int:

@@ -24,6 +24,7 @@ EXPORTS = (
     "qfa_blockmask_to_index",
     "qfa_attn_fwd",
     "qfa_attn_fwd_splitk",
+    "qfa_attn_fwd_unquant",
     "qfa_attn_split_workspace_bytes",
     "qfa_attn_splits_auto",
     "qfa_lse_merge",
@@ -61,6 +62,9 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_attn_fwd.restype = _I
     L.qfa_attn_fwd_splitk.argtypes = L.qfa_attn_fwd.argtypes[:-1] + [_I, _P, ctypes.c_size_t, _P]
     L.qfa_attn_fwd_splitk.restype = _I
+    L.qfa_attn_fwd_unquant.argtypes = ([_I64] * 6 + [_P, _I64, _I64, _I64] * 2 + [_P, _I, _I64, _I64, _I64]
+                                       + L.qfa_attn_fwd.argtypes[16:-1] + [_I, _P, ctypes.c_size_t, _P])
+    L.qfa_attn_fwd_unquant.restype = _I
     L.qfa_attn_split_workspace_bytes.argtypes = [_I64] * 4 + [_I, ctypes.POINTER(ctypes.c_size_t)]
     L.qfa_attn_split_workspace_bytes.restype = _I
     L.qfa_attn_splits_auto.argtypes = [_I64] * 4 + [_I, ctypes.POINTER(_I)]

@@ -197,9 +197,20 @@ int qfa_attn_splits_auto(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int causa
 }
 
 namespace {
-int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-                  const int8_t* q8, const float* qs, const float* qmu,
-                  const int8_t* k8, const float* ks,
+// Q/K operands of an attention call: int8 codes and scales, or (qf != NULL)
+// the unquantized Q and K views in V's dtype
+struct QKSrc {
+  const int8_t* q8;
+  const float* qs;
+  const float* qmu;
+  const int8_t* k8;
+  const float* ks;
+  const void* qf;
+  const void* kf;
+  int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss;
+};
+
+int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, const QKSrc& qk,
                   const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                   float sm_scale,
                   const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
@@ -213,11 +224,23 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   if (v_dtype != QFA_BF16 && v_dtype != QFA_FP16)
     return fail(v_dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "V dtype %d (supported: bf16, fp16)", v_dtype);
   if (B * H * Sq == 0) return ok();  // no output rows: empty tensors may have NULL data
-  if (!q8 || !qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs is NULL");
-  if (!aligned16(q8)) return fail(QFA_ERR_INVALID_ARG, "q8 must be 16-byte aligned");
+  const bool unquant = qk.qf != nullptr;
+  if (unquant) {
+    if ((st = check_view("q", qk.qf, v_dtype, qk.q_sb, qk.q_sh, qk.q_ss))) return st;
+  } else {
+    if (!qk.q8 || !qk.qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs is NULL");
+    if (!aligned16(qk.q8)) return fail(QFA_ERR_INVALID_ARG, "q8 must be 16-byte aligned");
+  }
   if (Sk > 0) {  // with no keys every row is fully masked and K/V are never read
-    if (!k8 || !ks) return fail(QFA_ERR_INVALID_ARG, "k8/ks is NULL");
-    if (!aligned16(k8)) return fail(QFA_ERR_INVALID_ARG, "k8 must be 16-byte aligned");
+    if (unquant) {
+      if ((st = check_view("k", qk.kf, v_dtype, qk.k_sb, qk.k_sh, qk.k_ss))) return st;
+      if (qk.k_ss >= (1ll << 24))
+        return fail(QFA_ERR_UNSUPPORTED, "K sequence stride %lld elements (supported: below 2^24)",
+                    (long long)qk.k_ss);
+    } else {
+      if (!qk.k8 || !qk.ks) return fail(QFA_ERR_INVALID_ARG, "k8/ks is NULL");
+      if (!aligned16(qk.k8)) return fail(QFA_ERR_INVALID_ARG, "k8 must be 16-byte aligned");
+    }
     if ((st = check_view("v", v, v_dtype, v_sb, v_sh, v_ss))) return st;
     // one 64-key tile of V then spans less than 2^31 bytes (32-bit copy ranges)
     if (v_ss >= (1ll << 24))
@@ -279,7 +302,12 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   a.nseg = nseg;
   a.causal = causal ? 1 : 0;
   a.B = (int)B; a.H = (int)H; a.Hkv = (int)Hkv; a.Sq = (int)Sq; a.Sk = (int)Sk; a.D = (int)D;
-  a.q8 = q8; a.qs = qs; a.qmu = qmu; a.k8 = k8; a.ks = ks;
+  if (unquant) {
+    a.qf = qk.qf; a.kf = qk.kf;
+    a.q_sb = qk.q_sb; a.q_sh = qk.q_sh; a.q_ss = qk.q_ss; a.k_sb = qk.k_sb; a.k_sh = qk.k_sh; a.k_ss = qk.k_ss;
+  } else {
+    a.q8 = qk.q8; a.qs = qk.qs; a.qmu = qk.qmu; a.k8 = qk.k8; a.ks = qk.ks;
+  }
   a.v = v; a.v_dtype = v_dtype; a.v_sb = v_sb; a.v_sh = v_sh; a.v_ss = v_ss;
   a.sm_scale = sm_scale;
   a.bias = bias; a.bias_dtype = bias_dtype; a.bias_sb = bias_sb; a.bias_sh = bias_sh;
@@ -306,7 +334,8 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
                  const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                  float* lse, void* stream) {
-  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, q8, qs, qmu, k8, ks, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
+  const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
                        bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, 1, nullptr, 0, stream);
 }
@@ -321,7 +350,25 @@ int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
                         const float* v_scale, int nseg, const int64_t* seg, int causal,
                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, q8, qs, qmu, k8, ks, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
+  const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
+                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                         const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                         const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                         const void* v, int dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                         float sm_scale,
+                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                         const int32_t* index, const int32_t* count, const int32_t* vbs,
+                         const float* v_scale, int nseg, const int64_t* seg, int causal,
+                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
+                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  const QKSrc qk{nullptr, nullptr, nullptr, nullptr, nullptr, q, k, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  if (!q && B * H * Sq > 0) return fail(QFA_ERR_INVALID_ARG, "q is NULL");
+  return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, dtype, v_sb, v_sh, v_ss, sm_scale,
                        bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
 }

@@ -165,15 +165,16 @@ __device__ __forceinline__ float xsum32(float x) {
 // lane after lane, from a wave-uniform LDS base). Rows are therefore stored
 // unpadded, and bank conflicts of the operand reads are avoided by XOR-ing
 // the 16-byte chunk index with a function of the row:
-//  K8 rows (D bytes, D/16 chunks): the MFMA A-operand read hands 16 lanes 16
-//    rows of one chunk; chunk ^= (row / (256/D)) mod (D/16) puts them on 16
-//    different 16-byte bank groups.
+//  K rows (R = D bytes of int8 codes, or 2D bytes of bf16/fp16 for the
+//    unquantized path; R/16 chunks): the MFMA A-operand read hands 16 lanes
+//    16 rows of one chunk; chunk ^= (row / (256/R)) mod (R/16) puts them on
+//    16 different 16-byte bank groups.
 //  V rows (2D bytes, D/8 chunks): ds_read_b64_tr_b16 hands a 16-lane group
 //    4 consecutive rows of one 32-byte window; chunk ^= (row mod 4) *
 //    (D/32) moves the 4 windows apart.
-template <int D>
+template <int R>
 __device__ __forceinline__ int k_chunk_pos(int row, int chunk) {
-  constexpr int kChunks = D / 16, kRowsPer256 = 256 / D;
+  constexpr int kChunks = R / 16, kRowsPer256 = 256 / R;
   return chunk ^ ((row / kRowsPer256) & (kChunks - 1));
 }
 template <int D>
@@ -345,15 +346,28 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 // cross the block's diagonal run in a loop of their own that sets the scores
 // of keys past the row to -inf, so the main loop is the plain one. Blocks
 // run heaviest first.
-template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false, bool CAUSAL = false>
+//
+// QB instances compute Q K^T on the unquantized bf16/fp16 Q and K (the type
+// of V) with the bf16/fp16 MFMA, accumulating from 0 in fp32; the key terms
+// are then ks = 1 and 0/-inf, the row factor sm_scale*log2(e), and the rest
+// of the tile is the same code. Their K tiles take 2D bytes per row: at
+// D = 128 a 3-stage ring (101 KB) would hold one block per CU, whose
+// register budget the compiler then fills with AGPRs copied to VGPRs on
+// every tile, so these instances use 2 stages (67 KB, two blocks per CU):
+// tile j copies K(j+2), V(j+1) and the raw terms of tile j+2, and ends
+// waiting for all of them (one tile of lead instead of two).
+template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false, bool CAUSAL = false,
+          bool QB = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
-  constexpr int KC = D / 32;                     // int8 MFMA k-steps / 32-channel blocks
-  constexpr int NSTG = 3;                        // LDS stages
-  constexpr int K_BYTES = BN * D, V_BYTES = BN * 2 * D;
+  constexpr int KC = D / 32;                     // 32-channel blocks of O
+  constexpr int NSTG = (QB && D == 128) ? 2 : 3; // LDS stages
+  constexpr int KROW = QB ? 2 * D : D;           // bytes per K row in LDS
+  constexpr int QSTEPS = QB ? D / 16 : D / 32;   // QK MFMA k-steps (16 bytes of Q per lane each)
+  constexpr int K_BYTES = BN * KROW, V_BYTES = BN * 2 * D;
   constexpr int KI = K_BYTES / 1024, VI = V_BYTES / 1024;   // 1 KB copy instructions per tile
   constexpr int KI_W = KI / NW, VI_W = VI / NW;            // ... per wave
-  constexpr int K_ROWS_I = 1024 / D, V_ROWS_I = 1024 / (2 * D);   // rows per copy instruction
+  constexpr int K_ROWS_I = 1024 / KROW, V_ROWS_I = 1024 / (2 * D);   // rows per copy instruction
   constexpr int N_COPY_W = KI_W + (DUMP ? 0 : VI_W);      // copy instructions per wave per tile
   static_assert(KI % NW == 0 && VI % NW == 0, "copy split");
   typedef typename std::conditional<VT == BF16, v8bf, v8h>::type pvec;
@@ -454,27 +468,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     }
   };
 
-  // ---- Q codes for this lane's row: kept in VGPRs for the whole key loop ----
-  v4i qreg[KC];
+  // ---- Q codes (QB: Q values) of this lane's row: kept in VGPRs for the
+  // whole key loop; 16 bytes per QK k-step ----
+  v4i qreg[QSTEPS];
+  const uint16_t* qsrc = QB ? (const uint16_t*)a.qf + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)q * a.q_ss)
+                            : nullptr;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    if (qvalid) qreg[c] = *(const v4i*)(a.q8 + qrow * D + 32 * c + 16 * hl);
-    else qreg[c] = v4i{0, 0, 0, 0};
+  for (int c = 0; c < QSTEPS; ++c) {
+    if (!qvalid) qreg[c] = v4i{0, 0, 0, 0};
+    else if (QB) qreg[c] = *(const v4i*)(qsrc + 16 * c + 8 * hl);
+    else qreg[c] = *(const v4i*)(a.q8 + qrow * D + 32 * c + 16 * hl);
   }
   // row factor of the log2-domain logits; kept above zero so that an
   // excluded key (-inf) stays -inf when scaled (a zero row's logits are 0
   // either way)
-  const float crow = DUMP ? 1.0f : fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f);
+  const float crow = DUMP ? 1.0f
+                          : (QB ? a.sm_scale * kLog2e
+                                : fmaxf(qvalid ? a.qs[qrow] * (a.sm_scale * kLog2e) : 0.0f, 1e-30f));
 
   // ---- per-(b,h) sources; every copy and load is range-checked. K8, key
   // scales and V come from the K/V head of this query head (grouped-query
   // calls share one among H / Hkv consecutive query heads) ----
   const int hk = h / (a.H / a.Hkv);
   const int64_t bhk = (int64_t)b * a.Hkv + hk;
-  const unsigned char* kbase = (const unsigned char*)(a.k8 + bhk * a.Sk * D);
+  const unsigned char* kbase =
+      QB ? (const unsigned char*)a.kf + ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh) * 2
+         : (const unsigned char*)(a.k8 + bhk * a.Sk * D);
+  const int k_row = QB ? (int)(a.k_ss * 2) : D;   // source bytes per K row (below 2^25, checked by the caller)
   const unsigned char* vbase = (const unsigned char*)a.v + ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh) * 2;
   const int v_row = (int)(a.v_ss * 2);   // below 2^25 (checked by the caller)
-  const float* ksbase = a.ks + bhk * a.Sk;
+  const float* ksbase = QB ? nullptr : a.ks + bhk * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
   // unbiased instances take a [1,1,1,K] keep mask (bool bytes) through the
@@ -486,9 +509,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 #pragma unroll
   for (int i = 0; i < KI_W; ++i) {
     const int ins = wave + i * NW;
-    const int row = ins * K_ROWS_I + lane / (D / 16), pos = lane % (D / 16);
+    const int row = ins * K_ROWS_I + lane / (KROW / 16), pos = lane % (KROW / 16);
     // LDS chunk `pos` of this row holds source chunk c with k_chunk_pos(row, c) == pos
-    k_src[i] = row * D + k_chunk_pos<D>(row, pos) * 16;
+    k_src[i] = row * k_row + k_chunk_pos<KROW>(row, pos) * 16;
   }
 #pragma unroll
   for (int i = 0; i < VI_W; ++i) {
@@ -503,7 +526,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   auto copy_k = [&](int stage, int tile, int valid) __attribute__((always_inline)) {
     const int key0 = tile * BN;
     const int rows = valid ? min(BN, a.Sk - key0) : 0;
-    const v4u d = buf_desc32(kbase + (int64_t)key0 * D, rows * D);
+    const v4u d = buf_desc32(kbase + (int64_t)key0 * k_row, rows > 0 ? (rows - 1) * k_row + KROW : 0);
 #pragma unroll
     for (int i = 0; i < KI_W; ++i) lds_copy<16>(lds_addr(&kbuf[stage][(wave + i * NW) * 1024]), k_src[i], d);
   };
@@ -524,7 +547,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     const int nk = valid ? hi - lo : 0;
     const int rel = tile * BN + lane - lo;   // negative offsets wrap and read as out of range
     if (wave == 0) {
-      lds_copy<4>(lds_addr(&kt[stage].raw[0][0]), rel * 4, buf_desc32(ksbase + lo, nk * 4));
+      if (!QB) lds_copy<4>(lds_addr(&kt[stage].raw[0][0]), rel * 4, buf_desc32(ksbase + lo, nk * 4));
     } else if (HAS_BIAS && wave == 1) {
       const v4u d = buf_desc32((const unsigned char*)a.bias + (bias_off + lo) * bias_esz, nk * bias_esz);
       if (bias_esz == 4) lds_copy<4>(lds_addr(&kt[stage].raw[1][0]), rel * 4, d);
@@ -542,14 +565,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     const int key = tile * BN + lane;
     const bool in = key >= lo && key < hi;
     if (wave == 0) {
-      const float ks = in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f;
+      // QB: unscaled fp32 scores, ks = 1 and no accumulator seed
+      const float ks = QB ? 1.0f : (in ? __uint_as_float(kt[stage].raw[0][lane]) : 0.0f);
+      const float seed = QB ? 0.0f : -kMagic * ks;
       kt[stage].sc[0][lane] = ks;
-      // an excluded key dequantizes to fma(x, 0, -inf) = -inf; a keep mask
+      // an excluded key dequantizes to fma(x, ks, -inf) = -inf; a keep mask
       // (copied by wave 1) excludes its zero entries the same way
       const bool keep = HAS_BIAS || !keep_mask || kt[stage].raw[1][lane] != 0u;
       const bool in_a = in && keep && (!SPARSE || (flags & 2));
-      kt[stage].sc[1][lane] = in_a ? -kMagic * ks : -INFINITY;
-      if (SPARSE) kt[stage].sc[3][lane] = in && (flags & 4) ? -kMagic * ks : -INFINITY;
+      kt[stage].sc[1][lane] = in_a ? seed : -INFINITY;
+      if (SPARSE) kt[stage].sc[3][lane] = in && (flags & 4) ? seed : -INFINITY;
     } else if (HAS_BIAS && wave == 1) {
       const uint32_t r = kt[stage].raw[1][lane];
       const float bias = a.bias_dtype == FP32 ? __uint_as_float(r)
@@ -571,15 +596,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const int tr_byte = 2 * (16 * (grp % 2) + 4 * (sl % 4));  // ... and byte inside a 64-byte channel block
 
   // S^T = K8 Q8^T of one 32-key block; accumulators start at kMagicBits
+  // (QB: S^T = K Q^T in fp32 from 0, its bits held in the same registers)
   v16i s[2];
   auto qk_block = [&](int stage, int blk) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[blk][r] = kMagicBits;
+    for (int r = 0; r < 16; ++r) s[blk][r] = QB ? 0 : kMagicBits;
     const int row = 32 * blk + lane % 32;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const v4i kv = *(const v4i*)(&kbuf[stage][row * D + k_chunk_pos<D>(row, 2 * c + hl) * 16]);
-      s[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qreg[c], s[blk], 0, 0, 0);
+    for (int c = 0; c < QSTEPS; ++c) {
+      const v4i kv = *(const v4i*)(&kbuf[stage][row * KROW + k_chunk_pos<KROW>(row, 2 * c + hl) * 16]);
+      if constexpr (!QB) {
+        s[blk] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kv, qreg[c], s[blk], 0, 0, 0);
+      } else if constexpr (VT == BF16) {
+        s[blk] = __builtin_bit_cast(v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(v8bf, kv), __builtin_bit_cast(v8bf, qreg[c]), __builtin_bit_cast(v16f, s[blk]), 0, 0, 0));
+      } else {
+        s[blk] = __builtin_bit_cast(v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(v8h, kv), __builtin_bit_cast(v8h, qreg[c]), __builtin_bit_cast(v16f, s[blk]), 0, 0, 0));
+      }
     }
   };
 
@@ -606,15 +640,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     // every wave's reads of K(0) are done before stage 0 is refilled
     stage_barrier<0>();
     next_tile(t2, l2, h2, v2);
-    copy_k(2, t2, v2);
-    copy_v(1, t1, v1);
+    if constexpr (NSTG == 3) {
+      copy_k(2, t2, v2);
+      copy_v(1, t1, v1);
+    }
   }
 
   // One tile. Excluded keys (segment edges, pad keys of block-sparse tiles)
   // carry -inf in their key terms, so every tile runs the same code.
   // `diag` (a literal at each call): the tile may hold keys past some row
   auto tile_body = [&](int iter, int st0, int st1, int st2, bool diag) __attribute__((always_inline)) {
-    // st0 = iter % 3, st1 = (iter + 1) % 3, st2 = (iter + 2) % 3
+    // st0 = iter % NSTG, st1 = (iter + 1) % NSTG, st2 = (iter + 2) % NSTG
     const KeyTerms& tc = kt[st0];
     int t3, l3, h3, v3;
     next_tile(t3, l3, h3, v3);
@@ -639,7 +675,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
           }
         qk_block(st1, blk);
       }
-      copy_k(iter % 3, t3, v3);
+      copy_k(st0, t3, v3);
       wait_vmcnt<N_COPY_W>();
       stage_barrier<N_COPY_W>();
       t1 = t2;
@@ -672,9 +708,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
         }
       }
       qk_block(st1, blk);   // the score registers of this block are free again
-      if (blk == 0) copy_k(iter % 3, t3, v3);   // K(iter+3) over K(iter)
+      if (blk == 0) {
+        if constexpr (NSTG == 3) copy_k(st0, t3, v3);   // K(iter+3) over K(iter)
+        else copy_k(st0, t2, v2);                       // K(iter+2) over K(iter)
+      }
     }
-    copy_v(st2, t2, v2);                        // V(iter+2) over V(iter-1)
+    if constexpr (NSTG == 3) copy_v(st2, t2, v2);      // V(iter+2) over V(iter-1)
+    else copy_v(st1, t1, v1);                          // V(iter+1) over V(iter-1)
     if (CAUSAL && diag) {
       // the walk is the single segment [0, Sk), so tile it0 + iter holds keys
       // (it0 + iter)*BN + [0, BN); only waves whose first row lies before the
@@ -760,10 +800,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
       }
     }
 
-    // ===== C: this wave's copies older than this tile's K/V copies are done;
-    // barrier =====
-    wait_vmcnt<N_COPY_W>();
-    stage_barrier<N_COPY_W>();
+    // ===== C: this wave's copies older than this tile's K/V copies are done
+    // (2 stages: all of them); barrier =====
+    constexpr int kLag = NSTG == 3 ? N_COPY_W : 0;
+    wait_vmcnt<kLag>();
+    stage_barrier<kLag>();
     t1 = t2;
     l1 = l2;
     h1 = h2;
@@ -781,22 +822,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   // it (from INT32_MAX) only when its lists run out.
   // (loop counts are relative to it0; n_tiles is a walk position)
   const int n_plain = CAUSAL ? max(0, min(n_tiles, (qt * BM + 1) / BN) - it0) : 0;
-  int st0 = 0, st1 = 1, st2 = 2;
+  int st0 = 0, st1 = 1, st2 = 2 % NSTG;
+  auto rotate = [&]() __attribute__((always_inline)) {
+    const int tmp = st0;
+    st0 = st1;
+    st1 = NSTG == 3 ? st2 : tmp;
+    st2 = NSTG == 3 ? tmp : st0;
+  };
   int iter = 0;
   for (; iter < (CAUSAL ? n_plain : n_tiles - it0); ++iter) {
     tile_body(iter, st0, st1, st2, false);
-    const int tmp = st0;
-    st0 = st1;
-    st1 = st2;
-    st2 = tmp;
+    rotate();
   }
   if constexpr (CAUSAL) {
     for (; iter < n_tiles - it0; ++iter) {
       tile_body(iter, st0, st1, st2, true);
-      const int tmp = st0;
-      st0 = st1;
-      st1 = st2;
-      st2 = tmp;
+      rotate();
     }
   }
   // drain this wave's remaining copies (they target stages nobody reads)
@@ -821,7 +862,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 }
 
 
-template <int D, int VT>
+template <int D, int VT, bool QB>
 hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   const bool sparse = a.index != nullptr;
   const int qtiles = (a.Sq + 127) / 128;   // 128 query rows (two 64-query tiles) per block
@@ -830,31 +871,37 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   if (total == 0) return hipSuccess;
   // split partials always carry their LSE
   const bool lse = a.lse != nullptr || ns > 1;
+  constexpr bool F = false, T = true;
   if (sparse) {
-    if (lse) attn_fwd_kernel<D, VT, 4, true, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
-    else attn_fwd_kernel<D, VT, 4, true, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, T, F, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, T, F, F, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
   } else if (a.causal) {
     // a keep mask (bool bias) runs in the unbiased instance; the grid pads
     // the (head, split) units to a multiple of 8 (see causal_order)
     const int total8 = qtiles * ((a.B * a.H * ns + 7) / 8 * 8);
     if (a.bias && a.bias_dtype != BOOL) {
-      if (lse) attn_fwd_kernel<D, VT, 4, false, true, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
-      else attn_fwd_kernel<D, VT, 4, false, true, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, T, T, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      else attn_fwd_kernel<D, VT, 4, F, T, F, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
     } else {
-      if (lse) attn_fwd_kernel<D, VT, 4, false, false, true, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
-      else attn_fwd_kernel<D, VT, 4, false, false, false, false, true><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
     }
   } else if (a.bias && a.bias_dtype != BOOL) {
-    if (lse) attn_fwd_kernel<D, VT, 4, false, true, true><<<total, 256, 0, s>>>(a, qtiles, total);
-    else attn_fwd_kernel<D, VT, 4, false, true, false><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, F, T, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, F, T, F, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
   } else {
-    if (lse) attn_fwd_kernel<D, VT, 4, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
-    else attn_fwd_kernel<D, VT, 4, false, false, false><<<total, 256, 0, s>>>(a, qtiles, total);
+    if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
+    else attn_fwd_kernel<D, VT, 4, F, F, F, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   CombineArgs c{a.B, a.H, a.Sq, D, ns, a.part_o, a.part_lse, a.out, a.out_dtype, a.o_sb, a.o_sh, a.o_ss, a.lse};
   return launch_split_combine(c, s);
+}
+
+template <int D, int VT>
+hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
+  return a.qf ? launch_d_vt<D, VT, true>(a, s) : launch_d_vt<D, VT, false>(a, s);
 }
 
 template <int D>

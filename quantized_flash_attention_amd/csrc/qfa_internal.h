@@ -53,6 +53,11 @@ struct AttnArgs {
   const float* qmu;     // nullable
   const int8_t* k8;
   const float* ks;
+  // unquantized Q K^T (qf != nullptr): Q [B,H,Sq,D] and K [B,Hkv,Sk,D] of
+  // v_dtype with element strides; q8, qs, qmu, k8, ks are then unused
+  const void* qf;
+  const void* kf;
+  int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss;
   const void* v;
   int v_dtype;
   int64_t v_sb, v_sh, v_ss;

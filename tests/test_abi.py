@@ -107,6 +107,24 @@ def test_split_rejects_bad_arguments():
     assert _attn_split(4, D=80) == _lib.QFA_ERR_UNSUPPORTED   # the plain checks still apply
 
 
+def _attn_unquant(dtype=1, q=FAKE, k=FAKE, q_s=(32768, 16384, 128), k_s=(32768, 16384, 128), Sk=128, ns=1):
+    st = (32768, 16384, 128)
+    return _lib.lib().qfa_attn_fwd_unquant(1, 2, 2, 128, Sk, 128, q, *q_s, k, *k_s, FAKE, dtype, *st,
+                                           ctypes.c_float(0.088), None, 3, 0, 0, None, None, None, None, 0, None, 0,
+                                           FAKE, 1, *st, None, ns, None, 0, None)
+
+
+def test_unquant_rejects_bad_arguments():
+    assert _attn_unquant(dtype=3) == _lib.QFA_ERR_UNSUPPORTED                     # fp32 Q/K/V
+    assert _attn_unquant(q=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn_unquant(k=None) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn_unquant(q=ctypes.c_void_p(0x10008)) == _lib.QFA_ERR_INVALID_ARG  # misaligned
+    assert _attn_unquant(k_s=(32768, 16384, 100)) == _lib.QFA_ERR_INVALID_ARG     # row stride not 16 bytes
+    assert _attn_unquant(k_s=(1 << 40, 1 << 32, 1 << 24)) == _lib.QFA_ERR_UNSUPPORTED
+    assert _attn_unquant(ns=2) == _lib.QFA_ERR_INVALID_ARG                       # split without workspace
+    assert _attn_unquant(q=None, k=None, Sk=0) == _lib.QFA_ERR_INVALID_ARG       # rows still need Q
+
+
 def _segs(*pairs):
     flat = [x for p in pairs for x in p]
     return (ctypes.c_int64 * len(flat))(*flat)
