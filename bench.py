@@ -410,6 +410,28 @@ def other_configs(dev) -> int:
         del q, k, v, qk, out, lse, ws
         torch.cuda.empty_cache()
 
+    # dense4k with a materialised per-query bias [1,1,Q,K] (the slow path) against the shared
+    # per-key bias [1,1,1,K] and no bias
+    w = W.WORKLOADS["dense4k"]
+    q_np, k_np, v_np = W.make_qkv(w)
+    q, k, v = up(q_np), up(k_np), up(v_np)
+    qk = qfa.quantize_qk(q, k)
+    out = torch.empty_like(q)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    b_key = torch.randn((1, 1, 1, w.Sk), generator=gen, device=dev)
+    b_f32 = torch.randn((1, 1, w.Sq, w.Sk), generator=gen, device=dev)
+    b_bf16 = b_f32.to(torch.bfloat16)
+    b_bool = b_f32 > -1.0
+    line = {"config": "dense4k_bias_forms", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} bf16"}
+    for name, b in (("none", None), ("per_key_fp32", b_key), ("per_query_fp32", b_f32),
+                    ("per_query_bf16", b_bf16), ("per_query_bool", b_bool)):
+        line[name + "_ms"] = round(_time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=b, out=out), 20), 4)
+    line["device"] = info
+    print(json.dumps(line), flush=True)
+    del q, k, v, qk, out, b_key, b_f32, b_bf16, b_bool
+    torch.cuda.empty_cache()
+
     # the causal shapes of ROCm/FlyDSL PR #886's timed table, (B, S, H, Hkv, D) and its FlyDSL
     # +LSE latency in us (bf16 QK on an MI350X: context, not a target); TFLOPS as that table
     # counts them, half of 4*B*H*S*S*D

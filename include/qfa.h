@@ -166,6 +166,15 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  *           masked key is excluded (-inf), so a row whose keys are all masked
  *           gets O = 0 and LSE = -inf. The mask is folded into the per-key
  *           terms and adds no per-score work.
+ * bias_sq:  0 for the shared per-key form above. Nonzero: a materialised
+ *           per-query bias or keep mask [B|1,H|1,Q,K] (comfy-kitchen issue
+ *           #177 passes such masks to attn_mask): element (b,h,i,j) at
+ *           bias + b*bias_sb + h*bias_sh + i*bias_sq + j, with bias_sq >= Sk;
+ *           base and the three strides 16-byte aligned in bytes, 32*bias_sq
+ *           elements below 2^31 bytes (else QFA_ERR_UNSUPPORTED). Values must
+ *           be finite or -inf. Each lane loads its row's 64 values per key
+ *           tile (the slow path: every score reads one bias value). Not with
+ *           unquantized Q/K (QFA_ERR_UNSUPPORTED).
  * index, count, vbs: block-sparse mode when index != NULL: int32 [B,H,T,T],
  *           int32 [B,H,T], int32 [T] (from qfa_blockmask_to_index; vbs may be
  *           NULL for full tiles), T = Sq/64 = Sk/64. Not combinable with bias.
@@ -193,7 +202,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
                  const int8_t* k8, const float* ks,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                  float sm_scale,
-                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                  const int32_t* index, const int32_t* count, const int32_t* vbs,
                  const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
@@ -244,7 +253,7 @@ int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
                         const int8_t* k8, const float* ks,
                         const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                         float sm_scale,
-                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                         const int32_t* index, const int32_t* count, const int32_t* vbs,
                         const float* v_scale, int nseg, const int64_t* seg, int causal,
                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
@@ -272,7 +281,7 @@ int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t 
                          const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
                          const void* v, int dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                          float sm_scale,
-                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                          const int32_t* index, const int32_t* count, const int32_t* vbs,
                          const float* v_scale, int nseg, const int64_t* seg, int causal,
                          void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,

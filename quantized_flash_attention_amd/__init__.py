@@ -156,12 +156,14 @@ def _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, unquant, v, sm_scale, bias, index,
     if return_lse and lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     _cont(lse, "lse", torch.float32)
-    bptr, bdt, bsb, bsh = None, QFA_FP32, 0, 0
+    bptr, bdt, bsb, bsh, bsq = None, QFA_FP32, 0, 0, 0
     if bias is not None:
         if bias.dim() != 4 or bias.shape[-1] != Sk or bias.stride(-1) != 1:
             raise ValueError("bias must be [B|1,H|1,Q|1,K] with a unit key stride")
-        if bias.shape[-2] != 1 and bias.stride(-2) != 0:
-            raise NotImplementedError("a materialised per-query bias is not supported; pass [..,1,K] or a stride-0 expansion")
+        if bias.shape[-2] not in (1, Sq):
+            raise ValueError("bias query dim must be 1 or Sq")
+        # a per-query bias (query stride != 0) takes the materialised path
+        bsq = bias.stride(-2) if bias.shape[-2] > 1 else 0
         if bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H):
             raise ValueError("bias batch/head dims must be 1 or match")
         bdt = QFA_BOOL if bias.dtype == torch.bool else _DT.get(bias.dtype)
@@ -177,7 +179,7 @@ def _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, unquant, v, sm_scale, bias, index,
         segs = [int(x) for pair in segments for x in pair]
         nseg = len(segs) // 2
         seg = (ctypes.c_int64 * max(1, len(segs)))(*segs)
-    masks = (ctypes.c_float(sm_scale), bptr, bdt, bsb, bsh, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale),
+    masks = (ctypes.c_float(sm_scale), bptr, bdt, bsb, bsh, bsq, _ptr(index), _ptr(count), _ptr(vbs), _ptr(v_scale),
              nseg, seg, int(bool(causal)), _ptr(out), do, *ost, _ptr(lse))
     ns = 1
     if splits == "auto":
@@ -208,10 +210,11 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
              lse: torch.Tensor | None = None, splits: int | str | None = None, workspace: torch.Tensor | None = None):
     """Attention on int8 Q/K codes (the dict from :func:`quantize_qk`) and bf16/fp16 V.
 
-    bias: per-key additive bias [B|1, H|1, 1|Q, K] (natural log) whose query
-        dimension is size 1 or a stride-0 expansion; fp32/bf16/fp16. A bool
-        tensor of that layout is a keep mask (True attends), applied through
-        the key terms at no per-score cost.
+    bias: additive bias [B|1, H|1, 1|Q, K] (natural log), fp32/bf16/fp16, or a bool
+        keep mask (True attends) of that layout. A query dimension of size 1 (or a
+        stride-0 expansion) is the shared per-key form, applied through the key terms
+        at no per-score cost; a materialised per-query one (int8 Q/K only; 16-byte
+        aligned rows) is read value by value, the slow path.
     index/count/vbs: block-sparse mode (from :func:`blockmask_to_index`).
     segments: up to 4 ascending disjoint (start, length) key ranges.
     causal: self-attention (Sq == Sk) where row i attends keys j <= i only.

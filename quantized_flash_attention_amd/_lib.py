@@ -57,7 +57,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_blockmask_to_index.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.qfa_blockmask_to_index.restype = _I
     L.qfa_attn_fwd.argtypes = ([_I64] * 6 + [_P] * 5 + [_P, _I, _I64, _I64, _I64] + [ctypes.c_float]
-                               + [_P, _I, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
+                               + [_P, _I, _I64, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
                                + [_P, _I, _I64, _I64, _I64] + [_P, _P])
     L.qfa_attn_fwd.restype = _I
     L.qfa_attn_fwd_splitk.argtypes = L.qfa_attn_fwd.argtypes[:-1] + [_I, _P, ctypes.c_size_t, _P]

@@ -29,7 +29,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
           "-I", os.path.join(ROOT, "include")]
 
 
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"]}
+# the attention kernel's assembly is kept (-save-temps=obj) for the check below
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans", "-save-temps=obj"]}
+ATTN_ASM = os.path.join(BUILD, "attn_fwd-hip-amdgcn-amd-amdhsa-gfx950.s")
 
 
 def _compile(src: str) -> str:
@@ -51,6 +53,12 @@ def build(jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # hand-issued bias loads: nothing may touch their registers before their wait
+    from .asm_check import check
+    bad = {k: v for k, v in check(ATTN_ASM).items() if v}
+    if bad:
+        os.remove(LIB) if os.path.exists(LIB) else None
+        raise RuntimeError(f"bias-load registers used before their wait: {bad}")
     os.replace(tmp, LIB)
     return LIB
 

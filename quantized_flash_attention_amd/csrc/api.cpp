@@ -75,7 +75,7 @@ int hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-int qfa_version(void) { return 200; }
+int qfa_version(void) { return 300; }
 
 const char* qfa_status_string(int status) {
   switch (status) {
@@ -213,7 +213,7 @@ struct QKSrc {
 int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, const QKSrc& qk,
                   const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                   float sm_scale,
-                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                   const int32_t* index, const int32_t* count, const int32_t* vbs,
                   const float* v_scale, int nseg, const int64_t* seg, int causal,
                   void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
@@ -254,8 +254,20 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   if (bias) {
     if (bias_dtype != QFA_FP32 && bias_dtype != QFA_BF16 && bias_dtype != QFA_FP16 && bias_dtype != QFA_BOOL)
       return fail(QFA_ERR_INVALID_ARG, "bias dtype %d", bias_dtype);
-    if (bias_sb < 0 || bias_sh < 0) return fail(QFA_ERR_INVALID_ARG, "negative bias stride");
+    if (bias_sb < 0 || bias_sh < 0 || bias_sq < 0) return fail(QFA_ERR_INVALID_ARG, "negative bias stride");
     if (index) return fail(QFA_ERR_INVALID_ARG, "bias and block-sparse mask are mutually exclusive");
+    if (bias_sq != 0) {
+      // materialised per-query bias: rows read 4 keys per 16-byte load
+      const int64_t esz = bias_dtype == QFA_FP32 ? 4 : (bias_dtype == QFA_BOOL ? 1 : 2);
+      if (unquant) return fail(QFA_ERR_UNSUPPORTED, "a per-query bias with unquantized Q/K");
+      if ((reinterpret_cast<uintptr_t>(bias) % 16) || (bias_sb * esz) % 16 || (bias_sh * esz) % 16 ||
+          (bias_sq * esz) % 16)
+        return fail(QFA_ERR_INVALID_ARG, "a per-query bias needs a 16-byte aligned base and row strides");
+      if (bias_sq < Sk) return fail(QFA_ERR_INVALID_ARG, "bias query stride %lld below Sk", (long long)bias_sq);
+      if (32 * bias_sq * esz >= (1ll << 31))
+        return fail(QFA_ERR_UNSUPPORTED, "bias query stride %lld elements (supported: 32 rows below 2^31 bytes)",
+                    (long long)bias_sq);
+    }
   }
   qfa::AttnArgs a{};
   if (index) {
@@ -310,7 +322,7 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   }
   a.v = v; a.v_dtype = v_dtype; a.v_sb = v_sb; a.v_sh = v_sh; a.v_ss = v_ss;
   a.sm_scale = sm_scale;
-  a.bias = bias; a.bias_dtype = bias_dtype; a.bias_sb = bias_sb; a.bias_sh = bias_sh;
+  a.bias = bias; a.bias_dtype = bias_dtype; a.bias_sb = bias_sb; a.bias_sh = bias_sh; a.bias_sq = bias ? bias_sq : 0;
   a.index = index; a.count = count; a.vbs = index ? vbs : nullptr;
   a.v_scale = v_scale;
   a.out = out; a.out_dtype = out_dtype; a.o_sb = o_sb; a.o_sh = o_sh; a.o_ss = o_ss;
@@ -329,14 +341,14 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
                  const int8_t* k8, const float* ks,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                  float sm_scale,
-                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                 const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                  const int32_t* index, const int32_t* count, const int32_t* vbs,
                  const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                  float* lse, void* stream) {
   const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
-                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, 1, nullptr, 0, stream);
 }
 
@@ -345,14 +357,14 @@ int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
                         const int8_t* k8, const float* ks,
                         const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                         float sm_scale,
-                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                        const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                         const int32_t* index, const int32_t* count, const int32_t* vbs,
                         const float* v_scale, int nseg, const int64_t* seg, int causal,
                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
-                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
 }
 
@@ -361,7 +373,7 @@ int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t 
                          const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
                          const void* v, int dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                          float sm_scale,
-                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh,
+                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
                          const int32_t* index, const int32_t* count, const int32_t* vbs,
                          const float* v_scale, int nseg, const int64_t* seg, int causal,
                          void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
@@ -369,7 +381,7 @@ int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t 
   const QKSrc qk{nullptr, nullptr, nullptr, nullptr, nullptr, q, k, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   if (!q && B * H * Sq > 0) return fail(QFA_ERR_INVALID_ARG, "q is NULL");
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, dtype, v_sb, v_sh, v_ss, sm_scale,
-                       bias, bias_dtype, bias_sb, bias_sh, index, count, vbs, v_scale, nseg, seg, causal,
+                       bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
 }
 

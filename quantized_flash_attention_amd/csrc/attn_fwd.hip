@@ -120,17 +120,6 @@ __device__ __forceinline__ void seg_at(const AttnArgs& a, int it, int& tile, int
   tile = t0 + it - base;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
-// 16-byte load through a buffer resource; offsets at or past the resource's
-// size read as zero (hardware range check), so tile tails need no branches.
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // max of 32 values as a tree of v_max3
@@ -356,8 +345,13 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 // every tile, so these instances use 2 stages (67 KB, two blocks per CU):
 // tile j copies K(j+2), V(j+1) and the raw terms of tile j+2, and ends
 // waiting for all of them (one tile of lead instead of two).
+//
+// BIAS2D instances (dense, int8 QK) add a materialised per-(query, key) bias
+// or bool keep mask [B|1,H|1,Q,K]: each lane loads its row's 32 values of the
+// tile (8 loads of 16 bytes, 4 keys each) at the start of the tile and adds
+// them after the dequantization, in natural-log units.
 template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false, bool CAUSAL = false,
-          bool QB = false>
+          bool QB = false, bool BIAS2D = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
   constexpr int BM = 32 * NW;
   constexpr int KC = D / 32;                     // 32-channel blocks of O
@@ -500,9 +494,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const float* ksbase = QB ? nullptr : a.ks + bhk * a.Sk;
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
+  // BIAS2D: one buffer descriptor over this wave's 32 rows of the bias (rows
+  // past Sq and bytes past the last row's key Sk - 1 read zero); the lane's
+  // row starts b2_row bytes in; the natural-log row factor qs*sm_scale
+  const int b2_esz = a.bias_dtype == FP32 ? 4 : (a.bias_dtype == BOOL ? 1 : 2);
+  v4u b2_desc = {0u, 0u, 0u, 0u};
+  int b2_row = 0;
+  float crow_nat = 0.0f;
+  if constexpr (BIAS2D) {
+    const int q0 = qt * BM + wave * 32;
+    const int nrow = max(0, min(32, a.Sq - q0));
+    b2_desc = buf_desc32((const unsigned char*)a.bias + (bias_off + (int64_t)q0 * a.bias_sq) * b2_esz,
+                         nrow > 0 ? (int)(((int64_t)(nrow - 1) * a.bias_sq + a.Sk) * b2_esz) : 0);
+    b2_row = (lane % 32) * (int)a.bias_sq * b2_esz;   // below 2^31 (checked by the caller)
+    crow_nat = fmaxf(qvalid ? a.qs[qrow] * a.sm_scale : 0.0f, 1e-30f);
+  }
   // unbiased instances take a [1,1,1,K] keep mask (bool bytes) through the
   // key terms: a masked key is excluded like a segment edge, at no per-score cost
-  const int keep_mask = (!HAS_BIAS && !SPARSE && !DUMP && a.bias != nullptr) ? 1 : 0;
+  const int keep_mask = (!HAS_BIAS && !BIAS2D && !SPARSE && !DUMP && a.bias != nullptr) ? 1 : 0;
 
   // per-lane source offsets of this wave's copy instructions (tile-relative)
   int k_src[KI_W], v_src[VI_W];
@@ -619,11 +628,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 
   // ---- prologue: K(0), K(1), V(0), the terms of tile 0 and the raw terms of
   // tile 1 in LDS; S(0) ----
+  int t0c;              // tile of the current iteration
   int t1, l1, h1, v1;   // tiles iter+1 and iter+2 of the loop below
   int t2, l2, h2, v2;   // (v: inside the walk)
   {
     int t0, l0, h0, v0;
     next_tile(t0, l0, h0, v0);
+    t0c = t0;
     next_tile(t1, l1, h1, v1);
     copy_terms(0, t0, l0, h0, v0);
     copy_terms(1, t1, l1, h1, v1);
@@ -652,6 +663,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   auto tile_body = [&](int iter, int st0, int st1, int st2, bool diag) __attribute__((always_inline)) {
     // st0 = iter % NSTG, st1 = (iter + 1) % NSTG, st2 = (iter + 2) % NSTG
     const KeyTerms& tc = kt[st0];
+    // BIAS2D: this tile's 32 bias values of the lane's row, 4 keys per load
+    // (keys 32 blk + 8 g + 4 hl + [0, 4) for load blk*4 + g), issued before
+    // the tile's copies; each block's four are waited for and added right
+    // after that block's dequantization (asm keeps the compiler from
+    // draining every copy before their first use)
+    v4u braw[8];
+    if constexpr (BIAS2D) {
+      const int kb = b2_row + (t0c * BN + 4 * hl) * b2_esz;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int off = kb + (32 * (i / 4) + 8 * (i % 4)) * b2_esz;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(braw[i]) : "v"(off), "s"(b2_desc) : "memory");
+      }
+    }
     int t3, l3, h3, v3;
     next_tile(t3, l3, h3, v3);
     copy_terms(st2, t2, l2, h2, v2);
@@ -707,6 +732,48 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
           for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(t[blk][4 * g + r], crow, bvs[r]);
         }
       }
+      if constexpr (BIAS2D) {
+        // block 0: at most loads 4..7 and the key-scale copy of wave 0 are
+        // newer; block 1: at most this tile's K copies. The registers are
+        // operands of the wait, so no read of them moves above it.
+        if (blk == 0) {
+          asm volatile("s_waitcnt vmcnt(4)" : "+v"(braw[0]), "+v"(braw[1]), "+v"(braw[2]), "+v"(braw[3]) :: "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(%4)" : "+v"(braw[4]), "+v"(braw[5]), "+v"(braw[6]), "+v"(braw[7])
+                       : "n"(KI_W) : "memory");
+        }
+        // t = S*ks*qs*sm_scale + bias (natural log; excluded keys stay -inf)
+        auto apply = [&](auto decode) __attribute__((always_inline)) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float bv[4];
+            decode(braw[4 * blk + g], bv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t[blk][4 * g + r] = fmaf(t[blk][4 * g + r], crow_nat, bv[r]);
+          }
+        };
+        if (a.bias_dtype == FP32) {
+          apply([](const v4u& w, float (&bv)[4]) {
+            bv[0] = __uint_as_float(w.x); bv[1] = __uint_as_float(w.y);
+            bv[2] = __uint_as_float(w.z); bv[3] = __uint_as_float(w.w);
+          });
+        } else if (a.bias_dtype == BOOL) {
+          apply([](const v4u& w, float (&bv)[4]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[r] = ((w.x >> (8 * r)) & 0xffu) ? 0.0f : -INFINITY;
+          });
+        } else if (a.bias_dtype == BF16) {
+          apply([](const v4u& w, float (&bv)[4]) {
+            bv[0] = bf16_bits_to_float(w.x & 0xffffu); bv[1] = bf16_bits_to_float(w.x >> 16);
+            bv[2] = bf16_bits_to_float(w.y & 0xffffu); bv[3] = bf16_bits_to_float(w.y >> 16);
+          });
+        } else {
+          apply([](const v4u& w, float (&bv)[4]) {
+            bv[0] = half_bits_to_float(w.x & 0xffffu); bv[1] = half_bits_to_float(w.x >> 16);
+            bv[2] = half_bits_to_float(w.y & 0xffffu); bv[3] = half_bits_to_float(w.y >> 16);
+          });
+        }
+      }
       qk_block(st1, blk);   // the score registers of this block are free again
       if (blk == 0) {
         if constexpr (NSTG == 3) copy_k(st0, t3, v3);   // K(iter+3) over K(iter)
@@ -731,8 +798,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
               if (32 * blk + 8 * g + 4 * hl + r > lim) t[blk][4 * g + r] = -INFINITY;
       }
     }
-    // crow > 0, so max(u)*crow = max(u*crow) (also for -inf)
-    const float mx = (HAS_BIAS) ? xmax32(max32(t)) : xmax32(max32(t)) * crow;
+    // crow > 0, so max(u)*crow = max(u*crow) (also for -inf); BIAS2D: t is
+    // in natural-log units
+    const float mx = HAS_BIAS ? xmax32(max32(t)) : xmax32(max32(t)) * (BIAS2D ? kLog2e : crow);
 
     // ---- lazy rescale: only when a row max passes the reference by the slack ----
     if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
@@ -758,6 +826,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
         if (HAS_BIAS) {
           x0 = t[blk][8 * m + 2 * e] - m_use;
           x1 = t[blk][8 * m + 2 * e + 1] - m_use;
+        } else if (BIAS2D) {
+          x0 = fmaf(t[blk][8 * m + 2 * e], kLog2e, -m_use);
+          x1 = fmaf(t[blk][8 * m + 2 * e + 1], kLog2e, -m_use);
         } else {
           x0 = fmaf(t[blk][8 * m + 2 * e], crow, -m_use);
           x1 = fmaf(t[blk][8 * m + 2 * e + 1], crow, -m_use);
@@ -805,6 +876,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     constexpr int kLag = NSTG == 3 ? N_COPY_W : 0;
     wait_vmcnt<kLag>();
     stage_barrier<kLag>();
+    t0c = t1;
     t1 = t2;
     l1 = l2;
     h1 = h2;
@@ -872,7 +944,17 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   // split partials always carry their LSE
   const bool lse = a.lse != nullptr || ns > 1;
   constexpr bool F = false, T = true;
-  if (sparse) {
+  if (!QB && !sparse && a.bias && a.bias_sq != 0) {
+    // materialised [B|1,H|1,Q,K] bias or keep mask
+    if (a.causal) {
+      const int total8 = qtiles * ((a.B * a.H * ns + 7) / 8 * 8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, F, T><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, F, T><<<total8, 256, 0, s>>>(a, qtiles, total8);
+    } else {
+      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, F, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
+      else attn_fwd_kernel<D, VT, 4, F, F, F, F, F, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
+    }
+  } else if (sparse) {
     if (lse) attn_fwd_kernel<D, VT, 4, T, F, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, T, F, F, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
   } else if (a.causal) {

@@ -65,6 +65,7 @@ struct AttnArgs {
   const void* bias;     // nullable; bias_dtype BOOL: a keep mask (nonzero bytes attend)
   int bias_dtype;
   int64_t bias_sb, bias_sh;
+  int64_t bias_sq;      // 0: one value per key shared by every query; else the query stride
   const int32_t* index; // nullable (dense)
   const int32_t* count;
   const int32_t* vbs;   // nullable

@@ -70,7 +70,7 @@ def _attn(**kw):
              out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
     a.update(kw)
     return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a.get("Hkv", a["H"]), a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
-                                   ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a["index"],
+                                   ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a.get("bsq", 0), a["index"],
                                    a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["causal"], a["out"], a["odt"],
                                    *a["o_s"], a["lse"], None)
 
@@ -82,7 +82,7 @@ def _attn_split(ns, ws=FAKE, wsb=1 << 30, **kw):
     a.update(kw)
     return _lib.lib().qfa_attn_fwd_splitk(a["B"], a["H"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"],
                                           a["vdt"], *a["v_s"], ctypes.c_float(a["scale"]), a["bias"], a["bdt"],
-                                          *a["b_s"], a["index"], a["count"], a["vbs"], a["vsc"], a["nseg"],
+                                          *a["b_s"], 0, a["index"], a["count"], a["vbs"], a["vsc"], a["nseg"],
                                           a["seg"], a["causal"], a["out"], a["odt"], *a["o_s"], a["lse"], ns, ws,
                                           wsb, None)
 
@@ -107,10 +107,11 @@ def test_split_rejects_bad_arguments():
     assert _attn_split(4, D=80) == _lib.QFA_ERR_UNSUPPORTED   # the plain checks still apply
 
 
-def _attn_unquant(dtype=1, q=FAKE, k=FAKE, q_s=(32768, 16384, 128), k_s=(32768, 16384, 128), Sk=128, ns=1):
+def _attn_unquant(dtype=1, q=FAKE, k=FAKE, q_s=(32768, 16384, 128), k_s=(32768, 16384, 128), Sk=128, ns=1,
+                  bias=None, bsq=0):
     st = (32768, 16384, 128)
     return _lib.lib().qfa_attn_fwd_unquant(1, 2, 2, 128, Sk, 128, q, *q_s, k, *k_s, FAKE, dtype, *st,
-                                           ctypes.c_float(0.088), None, 3, 0, 0, None, None, None, None, 0, None, 0,
+                                           ctypes.c_float(0.088), bias, 3, 0, 0, bsq, None, None, None, None, 0, None, 0,
                                            FAKE, 1, *st, None, ns, None, 0, None)
 
 
@@ -123,6 +124,7 @@ def test_unquant_rejects_bad_arguments():
     assert _attn_unquant(k_s=(1 << 40, 1 << 32, 1 << 24)) == _lib.QFA_ERR_UNSUPPORTED
     assert _attn_unquant(ns=2) == _lib.QFA_ERR_INVALID_ARG                       # split without workspace
     assert _attn_unquant(q=None, k=None, Sk=0) == _lib.QFA_ERR_INVALID_ARG       # rows still need Q
+    assert _attn_unquant(bias=FAKE, bsq=128) == _lib.QFA_ERR_UNSUPPORTED          # per-query bias
 
 
 def _segs(*pairs):
@@ -155,6 +157,13 @@ def test_attn_rejects_bad_arguments():
     assert b"Sq == Sk" in _lib.lib().qfa_last_error()
     assert _attn(causal=1, nseg=1, seg=_segs((0, 128))) == _lib.QFA_ERR_UNSUPPORTED
     assert _attn(causal=1, index=FAKE, count=FAKE) == _lib.QFA_ERR_UNSUPPORTED
+    # materialised per-query bias: alignment, stride >= Sk, 32-row span
+    assert _attn(bias=FAKE, bsq=-4) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(bias=FAKE, bsq=100) == _lib.QFA_ERR_INVALID_ARG                 # below Sk = 128
+    assert _attn(bias=FAKE, bsq=130) == _lib.QFA_ERR_INVALID_ARG                 # 520-byte rows
+    assert _attn(bias=ctypes.c_void_p(0x10008), bsq=128) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(bias=FAKE, bsq=1 << 24) == _lib.QFA_ERR_UNSUPPORTED
+    assert _attn(bias=FAKE, bsq=128, index=FAKE, count=FAKE) == _lib.QFA_ERR_INVALID_ARG
     # grouped-query heads: Hkv must divide H
     for hkv in (0, 3, 4, -1):
         assert _attn(Hkv=hkv) == _lib.QFA_ERR_INVALID_ARG
@@ -200,5 +209,5 @@ def test_python_binding_refuses_grad_and_bad_bias():
     qk = dict(q8=torch.zeros(1, 1, 64, 128, dtype=torch.int8), qs=torch.zeros(1, 1, 64),
               k8=torch.zeros(1, 1, 64, 128, dtype=torch.int8), ks=torch.zeros(1, 1, 64))
     v = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
-    with pytest.raises(NotImplementedError, match="per-query bias"):
-        qfa.attn_fwd(qk, v, bias=torch.zeros(1, 1, 64, 64))
+    with pytest.raises(ValueError, match="query dim"):
+        qfa.attn_fwd(qk, v, bias=torch.zeros(1, 1, 7, 64))

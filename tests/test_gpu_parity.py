@@ -500,6 +500,79 @@ def test_unquant_error_below_int8_error():
     assert eb.max() <= O_MAX_ABS
 
 
+def _bias2d(kind, B, H, Sq, Sk, seed):
+    """A materialised bias [B|1,H|1,Sq,Sk] (rows padded to a 16-byte multiple) as (numpy view for
+    the oracle, device view for the kernel)."""
+    rs = np.random.default_rng(seed)
+    esz = {"fp32": 4, "bf16": 2, "fp16": 2, "bool": 1}[kind]
+    pad = -(-Sk * esz // 16) * 16 // esz
+    if kind == "bool":
+        full = rs.random((B, H, Sq, pad)) < 0.7
+        view = full[..., :Sk]
+        ref = np.where(view, 0.0, -np.inf).astype(np.float32)
+        dev = torch.from_numpy(full).to(DEV)[..., :Sk]
+        return ref, dev
+    vals = (rs.standard_normal((B, H, Sq, pad)) * 2.0).astype(np.float32)
+    vals[rs.random(vals.shape) < 0.05] = -np.inf
+    if kind == "fp32":
+        full = vals
+    elif kind == "bf16":
+        full = W.f32_to_bf16_bits(vals)
+    else:
+        full = vals.astype(np.float16)
+    return full[..., :Sk], up(full)[..., :Sk]
+
+
+BIAS2D_CASES = {
+    # (workload, shape, bias kind, bias batch/head extents, options)
+    "fp32_ragged_padded_rows": ("dense4k", dict(H=2, Sq=333, Sk=517), "fp32", (1, 1), {}),
+    "bf16_per_batch_head": ("tiny", dict(B=2, H=2, Sq=200, Sk=300), "bf16", (2, 2), {}),
+    "fp16_per_head_gqa": ("dense4k", dict(H=4, Hkv=2, Sq=256, Sk=640), "fp16", (1, 4), {}),
+    "bool_keep_causal": ("dense4k", dict(H=2, Sq=517, Sk=517), "bool", (1, 1), {"causal": True}),
+    "fp32_split_3_no_lse": ("band", dict(H=2, Sq=200, Sk=2100), "fp32", (1, 2), {"splits": 3, "lse": False}),
+}
+
+
+@pytest.mark.parametrize("case", list(BIAS2D_CASES))
+def test_bias2d_parity(case):
+    """Materialised per-query bias / keep mask [B|1,H|1,Q,K] against the oracle."""
+    wn, shape, kind, (bb, bh), opt = BIAS2D_CASES[case]
+    w = W.WORKLOADS[wn]
+    q, k, v = W.make_qkv(w, **shape)
+    B, H, Sq, _ = q.shape
+    Sk = k.shape[2]
+    ref_b, dev_b = _bias2d(kind, bb, bh, Sq, Sk, seed=len(case))
+    if kind == "bool":
+        dev_b[..., 3, :] = False          # a row with nothing attended
+        ref_b[..., 3, :] = -np.inf
+    causal = opt.get("causal", False)
+    ref = oracle.quantize_qk(q, k)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, causal=causal)
+    g = gpu_quant(q, k)
+    lse = opt.get("lse", True)
+    res = qfa.attn_fwd(g, up(v), w.sm_scale, bias=dev_b, causal=causal, splits=opt.get("splits"), return_lse=lse)
+    o = res[0] if lse else res
+    check_o(o, o_ref, what=case)
+    if lse:
+        check_lse(res[1], l_ref, what=case)
+    if kind == "bool":
+        assert torch.all(o[:, :, 3] == 0)
+
+
+def test_bias2d_full_size_sampled():
+    """B1 H16 S4096 D128 with a materialised bf16 [1,1,4096,4096] bias, sampled rows."""
+    w = W.WORKLOADS["dense4k"]
+    q, k, v = W.make_qkv(w)
+    ref_b, dev_b = _bias2d("bf16", 1, 1, w.Sq, w.Sk, seed=7)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    rows = sample_rows(w.B, w.H, w.Sq, per_head=16)
+    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, bias=dev_b, return_lse=True)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, rows=rows)
+    check_o(o, o_ref, rows, "bias2d full")
+    check_lse(l, l_ref, rows, "bias2d full")
+
+
 def test_attn_deterministic():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=1024)
