@@ -298,8 +298,8 @@ int qfa_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t D, 
  * two up to 16; 1 when the unsplit grid already fills it): first enough
  * (query block, head, split) blocks for about one round of two per CU while
  * a split keeps at least 16 key tiles of the walk (causal calls: of the
- * average walk), then, for long walks, more splits while each keeps at least
- * 128 tiles, up to three rounds. Writes *num_splits.
+ * average walk), then, for long non-causal walks, more splits while each
+ * keeps at least 128 tiles, up to three rounds. Writes *num_splits.
  */
 int qfa_attn_splits_auto(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int causal, int* num_splits);
 

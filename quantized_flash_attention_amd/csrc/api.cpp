@@ -183,15 +183,17 @@ int qfa_attn_splits_auto(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int causa
   if ((st = hip_status(qfa::device_cu_count(&ncu), "device query"))) return st;
   // Powers of two only (odd counts measured slower). First fill about one
   // round of two blocks per CU while a split keeps >= 16 key tiles of the
-  // (causal: average) walk; then, for long walks, keep halving them while a
-  // split keeps >= 128 tiles, up to three rounds, so the last round's tail is
-  // short. Tuned on banded B1 H1..14 Sq1024..4096 Sk4096..33600 shapes.
+  // (causal: average) walk; then, for long non-causal walks, keep halving
+  // them while a split keeps >= 128 tiles, up to three rounds, so the last
+  // round's tail is short (causal grids are already ordered longest walk
+  // first, and splitting them measured no gain). Tuned on banded B1 H1..14
+  // Sq1024..4096 Sk4096..33600 and causal S2048..32768 shapes.
   const int64_t blocks = (Sq + 127) / 128 * B * H;
   const int64_t walk = causal ? ((Sk + 63) / 64 + 1) / 2 : (Sk + 63) / 64;
   const int64_t slots = 2 * (int64_t)std::max(ncu, 1);
   int64_t n = 1;
   while (n < 16 && blocks * n * 100 < 85 * slots && walk / (2 * n) >= 8) n *= 2;
-  while (n < 16 && blocks * n < 3 * slots && walk / n >= 128) n *= 2;
+  while (!causal && n < 16 && blocks * n < 3 * slots && walk / n >= 128) n *= 2;
   *num_splits = (int)n;
   return ok();
 }
@@ -283,9 +285,9 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   if (num_splits < 1 || num_splits > QFA_MAX_SPLITS)
     return fail(QFA_ERR_INVALID_ARG, "num_splits %d (1..%d)", num_splits, QFA_MAX_SPLITS);
   if (num_splits > 1 && index) return fail(QFA_ERR_UNSUPPORTED, "split-K with a block-sparse mask");
-  // one 128-row block per (query tile, head, split), padded to 8 units for
-  // causal calls; 256 threads per block keep the launch within 2^32 threads
-  if ((Sq + 127) / 128 * ((B * H * num_splits + 7) / 8 * 8) > (1ll << 24))
+  // one 128-row block per (query tile, head, split); 256 threads per block
+  // keep the launch within 2^32 threads
+  if ((Sq + 127) / 128 * B * H * num_splits > (1ll << 24))
     return fail(QFA_ERR_UNSUPPORTED, "more than 2^24 blocks of 128 query rows");
   if (num_splits > 1) {
     size_t need = 0;

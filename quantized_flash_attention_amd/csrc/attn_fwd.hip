@@ -82,13 +82,16 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 }
 
 // Causal launches: dispatch index k -> work index L. Work is numbered by
-// query-tile rank (longest walk first), then head, over a head count padded
-// to a multiple of 8, so that a head's blocks share one XCD (k mod 8) and
-// padding blocks exit at once. Blocks k and k + ncu start on the same CU, so
-// the second round of ncu blocks runs in reverse (in groups of 8, keeping
-// k mod 8): each CU then pairs a long walk with a short one. Any order is
-// correct; this one balances the first two rounds, and later blocks take
-// freed slots longest first.
+// query-tile rank (longest walk first), then (head, split) unit. Blocks k and
+// k + ncu start on the same CU, so the second round of ncu blocks runs in
+// reverse (in groups of 8, keeping k mod 8): each CU then pairs a long walk
+// with a short one. Block k runs on XCD k mod 8, so when the unit count is a
+// multiple of 8 a unit's blocks share one XCD (L mod 8 = unit mod 8);
+// otherwise the units rotate over the XCDs. (Padding the unit count to a
+// multiple of 8 would pin the padding to whole XCDs: with 4 units, XCDs 4..7
+// would get nothing but empty blocks.) Any order is correct; this one
+// balances the first two rounds, and later blocks take freed slots longest
+// first.
 __device__ __forceinline__ int causal_order(int k, int total, int ncu) {
   if (ncu % 8 != 0 || k < ncu || k >= 2 * ncu) return k;
   const int m = min(total, 2 * ncu) - ncu;   // blocks of the second round
@@ -375,10 +378,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   int bh, qt, split;
   if constexpr (CAUSAL) {
     const int L = causal_order((int)blockIdx.x, total_blocks, a.ncu);
-    const int u8 = total_blocks / qtiles;
-    const int unit = L % u8;
-    qt = qtiles - 1 - L / u8;
-    if (unit >= a.B * a.H * ns) return;   // unit padding: the whole block leaves before any barrier
+    const int units = total_blocks / qtiles;
+    const int unit = L % units;
+    qt = qtiles - 1 - L / units;
     bh = unit / ns;
     split = unit % ns;
   } else {
@@ -947,9 +949,8 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   if (!QB && !sparse && a.bias && a.bias_sq != 0) {
     // materialised [B|1,H|1,Q,K] bias or keep mask
     if (a.causal) {
-      const int total8 = qtiles * ((a.B * a.H * ns + 7) / 8 * 8);
-      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, F, T><<<total8, 256, 0, s>>>(a, qtiles, total8);
-      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, F, T><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
+      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
     } else {
       if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, F, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
       else attn_fwd_kernel<D, VT, 4, F, F, F, F, F, F, T><<<total, 256, 0, s>>>(a, qtiles, total);
@@ -958,15 +959,13 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
     if (lse) attn_fwd_kernel<D, VT, 4, T, F, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
     else attn_fwd_kernel<D, VT, 4, T, F, F, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
   } else if (a.causal) {
-    // a keep mask (bool bias) runs in the unbiased instance; the grid pads
-    // the (head, split) units to a multiple of 8 (see causal_order)
-    const int total8 = qtiles * ((a.B * a.H * ns + 7) / 8 * 8);
+    // a keep mask (bool bias) runs in the unbiased instance (block order: causal_order)
     if (a.bias && a.bias_dtype != BOOL) {
-      if (lse) attn_fwd_kernel<D, VT, 4, F, T, T, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
-      else attn_fwd_kernel<D, VT, 4, F, T, F, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, T, T, F, T, QB><<<total, 256, 0, s>>>(a, qtiles, total);
+      else attn_fwd_kernel<D, VT, 4, F, T, F, F, T, QB><<<total, 256, 0, s>>>(a, qtiles, total);
     } else {
-      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
-      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, QB><<<total8, 256, 0, s>>>(a, qtiles, total8);
+      if (lse) attn_fwd_kernel<D, VT, 4, F, F, T, F, T, QB><<<total, 256, 0, s>>>(a, qtiles, total);
+      else attn_fwd_kernel<D, VT, 4, F, F, F, F, T, QB><<<total, 256, 0, s>>>(a, qtiles, total);
     }
   } else if (a.bias && a.bias_dtype != BOOL) {
     if (lse) attn_fwd_kernel<D, VT, 4, F, T, T, F, F, QB><<<total, 256, 0, s>>>(a, qtiles, total);
