@@ -188,8 +188,9 @@ def main() -> int:
     flops_full = 4.0 * B * H * Sq * Sk * D
     tflops = lambda fl, ms: fl / (ms * 1e-3) / 1e12
     split_ms = med["core"] + med["skirt"] + med["merge"]
-    # algorithmic bytes of the quantize step: read Q and K once, write codes, scales, mean, centring term
-    qbytes = (B * H * (Sq + Sk) * D * 2 + B * H * (Sq + Sk) * D + B * H * (Sq + Sk) * 4
+    # algorithmic bytes of the quantize step: read K twice (the mean, then the codes) and Q once,
+    # write codes, scales, mean, centring term
+    qbytes = (B * H * (Sq + 2 * Sk) * D * 2 + B * H * (Sq + Sk) * D + B * H * (Sq + Sk) * 4
               + B * H * D * 4 + B * H * Sq * 4)
     mbytes = B * H * Sq * (2 * D * 4 + 2 * 4 + D * 2 + 4)
     step_flops = 3 * flops_full
@@ -385,8 +386,8 @@ def other_configs(dev) -> int:
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     def qbytes(B, H, Sq, Sk, D, esz):
-        # read Q and K once; write codes, scales, K mean, centring term
-        return B * H * (Sq + Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
+        # read K twice (the mean, then the codes) and Q once; write codes, scales, K mean, centring term
+        return B * H * (Sq + 2 * Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
 
     info = device_info(dev)
     for name in ("dense4k", "d64"):

@@ -109,6 +109,9 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, i
   if (dtype != QFA_BF16 && dtype != QFA_FP16)
     return fail(dtype == QFA_FP32 ? QFA_ERR_UNSUPPORTED : QFA_ERR_INVALID_ARG, "Q/K dtype %d (supported: bf16, fp16)", dtype);
   if (B * H == 0) return ok();  // nothing to read or write: empty tensors may have NULL data
+  // 1-D grids of 256-thread blocks over at least 64 rows each stay within 2^32 threads
+  if (B * H * Sq > (1ll << 30) || B * Hkv * Sk > (1ll << 30))
+    return fail(QFA_ERR_UNSUPPORTED, "more than 2^30 rows of Q or K");
   if (Sq > 0) {
     if ((st = check_view("q", q, dtype, q_sb, q_sh, q_ss))) return st;
     if (!q8 || !qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs output is NULL");
