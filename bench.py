@@ -40,12 +40,18 @@ PEAK_BLEND = 2.0 / (1.0 / PEAK_I8_TOPS + 1.0 / PEAK_BF16_TFLOPS)
 # int8_attention, first of the two runs): unmasked, fp32 bias, core+skirt.
 PAGE_MS = {"unmasked": 8.64, "bias_fp32": 15.28, "split_unmerged": 11.05}
 
-ATTN_SRC = os.path.join(ROOT, "quantized_flash_attention_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's sources: the template, its dispatch and its instance files
+ATTN_SRC = sorted(os.path.join(ROOT, "quantized_flash_attention_amd", "csrc", f)
+                  for f in os.listdir(os.path.join(ROOT, "quantized_flash_attention_amd", "csrc"))
+                  if f.startswith("attn_fwd"))
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_band_unmasked_pmc.json")
 
 
-def src_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(launch_key: str):

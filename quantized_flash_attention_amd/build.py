@@ -21,7 +21,10 @@ ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build", "qfa")
 LIB = os.path.join(PKG, "libqfa.so")
 
-SOURCES = ["quantize.hip", "attn_fwd.hip", "blockmask.hip", "lse_merge.hip", "api.cpp"]
+# the attention kernel's instances are split over four translation units compiled in parallel
+ATTN_INST = ["attn_fwd_inst_d128_bf16.hip", "attn_fwd_inst_d128_fp16.hip", "attn_fwd_inst_d64_bf16.hip",
+             "attn_fwd_inst_d64_fp16.hip"]
+SOURCES = ATTN_INST + ["quantize.hip", "attn_fwd.hip", "blockmask.hip", "lse_merge.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -30,8 +33,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
 
 
 # the attention kernel's assembly is kept (-save-temps=obj) for the check below
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans", "-save-temps=obj"]}
-ATTN_ASM = os.path.join(BUILD, "attn_fwd-hip-amdgcn-amd-amdhsa-gfx950.s")
+EXTRA = {src: ["-fno-honor-nans", "-save-temps=obj"] for src in ATTN_INST}
+EXTRA["attn_fwd.hip"] = ["-fno-honor-nans"]
+ATTN_ASM = [os.path.join(BUILD, os.path.splitext(src)[0] + "-hip-amdgcn-amd-amdhsa-gfx950.s") for src in ATTN_INST]
 
 
 def _compile(src: str) -> str:
@@ -55,7 +59,7 @@ def build(jobs: int = 8) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     # hand-issued bias loads: nothing may touch their registers before their wait
     from .asm_check import check
-    bad = {k: v for k, v in check(ATTN_ASM).items() if v}
+    bad = {k: v for asm in ATTN_ASM for k, v in check(asm).items() if v}
     if bad:
         os.remove(LIB) if os.path.exists(LIB) else None
         raise RuntimeError(f"bias-load registers used before their wait: {bad}")
