@@ -795,3 +795,44 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         for t, e in zip(outs, eager):
             assert torch.equal(t, e), f"replay {rep}: a captured output differs from the eager step"
+
+
+def test_graph_capture_replays_new_paths():
+    """Split-K (partials + combine), causal with GQA, the unquantized-QK path and a
+    materialised per-query keep mask, captured in one HIP graph with caller-provided
+    workspaces: every replay matches the eager results bit for bit."""
+    w = W.WORKLOADS["dense4k"]
+    S = 700
+    q, k, v = W.make_qkv(w, H=4, Hkv=2, Sq=S, Sk=S)
+    tq, tk, tv = up(q), up(k), up(v)
+    wsq = torch.empty(qfa.quantize_workspace_bytes(1, 2, S, 128), dtype=torch.uint8, device=DEV)
+    wss = torch.empty(qfa.split_workspace_bytes(1, 4, S, 128, 3), dtype=torch.uint8, device=DEV)
+    _, keep = _bias2d("bool", 1, 1, S, S, seed=2)    # rows padded to a 16-byte multiple
+
+    def step():
+        qk = qfa.quantize_qk(tq, tk, workspace=wsq)
+        o_s, l_s = qfa.attn_fwd(qk, tv, w.sm_scale, splits=3, workspace=wss, return_lse=True)
+        o_c, l_c = qfa.attn_fwd(qk, tv, w.sm_scale, causal=True, return_lse=True)
+        o_u = qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, causal=True)
+        o_k = qfa.attn_fwd(qk, tv, w.sm_scale, bias=keep)
+        return [qk["k8"], qk["qmu"], o_s, l_s, o_c, l_c, o_u, o_k]
+
+    eager = [t.clone() for t in step()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(t, e), f"replay {rep}: captured output {i} differs from the eager step"
