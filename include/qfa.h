@@ -173,8 +173,11 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  *           base and the three strides 16-byte aligned in bytes, 32*bias_sq
  *           elements below 2^31 bytes (else QFA_ERR_UNSUPPORTED). Values must
  *           be finite or -inf. Each lane loads its row's 64 values per key
- *           tile (the slow path: every score reads one bias value). Not with
- *           unquantized Q/K (QFA_ERR_UNSUPPORTED).
+ *           tile (the slow path: every score reads one bias value). The row
+ *           padding past key Sk - 1 may hold anything (NaN included): it is
+ *           read but never used; in the last row the read stops at the
+ *           4-byte boundary after key Sk - 1. Not with unquantized Q/K
+ *           (QFA_ERR_UNSUPPORTED).
  * index, count, vbs: block-sparse mode when index != NULL: int32 [B,H,T,T],
  *           int32 [B,H,T], int32 [T] (from qfa_blockmask_to_index; vbs may be
  *           NULL for full tiles), T = Sq/64 = Sk/64. Not combinable with bias.

@@ -499,8 +499,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   const int64_t bias_off = (int64_t)b * a.bias_sb + (int64_t)h * a.bias_sh;
   const int bias_esz = a.bias_dtype == FP32 ? 4 : 2;
   // BIAS2D: one buffer descriptor over this wave's 32 rows of the bias (rows
-  // past Sq and bytes past the last row's key Sk - 1 read zero); the lane's
-  // row starts b2_row bytes in; the natural-log row factor qs*sm_scale
+  // past Sq read zero); the lane's row starts b2_row bytes in; the
+  // natural-log row factor qs*sm_scale. A buffer load returns zero for every
+  // dword not wholly inside the range, so the range ends at the dword that
+  // holds the last row's key Sk - 1 (4-byte aligned, as rows start on
+  // 16-byte boundaries, so it never leaves the page of a valid byte); the
+  // bytes of keys past Sk are forced out in the tile that holds them
   const int b2_esz = a.bias_dtype == FP32 ? 4 : (a.bias_dtype == BOOL ? 1 : 2);
   v4u b2_desc = {0u, 0u, 0u, 0u};
   int b2_row = 0;
@@ -508,8 +512,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
   if constexpr (BIAS2D) {
     const int q0 = qt * BM + wave * 32;
     const int nrow = max(0, min(32, a.Sq - q0));
+    const int64_t tail = ((int64_t)a.Sk * b2_esz + 3) & ~(int64_t)3;
     b2_desc = buf_desc32((const unsigned char*)a.bias + (bias_off + (int64_t)q0 * a.bias_sq) * b2_esz,
-                         nrow > 0 ? (int)(((int64_t)(nrow - 1) * a.bias_sq + a.Sk) * b2_esz) : 0);
+                         nrow > 0 ? (int)((int64_t)(nrow - 1) * a.bias_sq * b2_esz + tail) : 0);
     b2_row = (lane % 32) * (int)a.bias_sq * b2_esz;   // below 2^31 (checked by the caller)
     crow_nat = fmaxf(qvalid ? a.qs[qrow] * a.sm_scale : 0.0f, 1e-30f);
   }
@@ -786,6 +791,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     }
     if constexpr (NSTG == 3) copy_v(st2, t2, v2);      // V(iter+2) over V(iter-1)
     else copy_v(st1, t1, v1);                          // V(iter+1) over V(iter-1)
+    if constexpr (BIAS2D) {
+      // keys past Sk (only in the tile that holds key Sk - 1) read row
+      // padding or the next row: excluded by their key terms, but a NaN or
+      // +inf there would make fma(-inf, c, bias) NaN. A bool byte decodes
+      // to 0 or -inf, so the keep-mask form needs nothing.
+      const int key0 = t0c * BN;
+      if (key0 + BN > a.Sk && a.bias_dtype != BOOL) {
+        const int lim = a.Sk - 1 - key0;   // last key of the row, tile-relative
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (32 * blk + 8 * g + 4 * hl + r > lim) t[blk][4 * g + r] = -INFINITY;
+      }
+    }
     if (CAUSAL && diag) {
       // the walk is the single segment [0, Sk), so tile it0 + iter holds keys
       // (it0 + iter)*BN + [0, BN); only waves whose first row lies before the

@@ -559,6 +559,42 @@ def test_bias2d_parity(case):
         assert torch.all(o[:, :, 3] == 0)
 
 
+@pytest.mark.parametrize("kind", ["bool", "bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("Sk", [461, 462, 463, 464])
+def test_bias2d_row_tail(kind, Sk):
+    """The last six keys of every row dominate (kept alone but for a few, or biased +6), so a
+    lost key Sk - 1 shows: its bytes share a dword with the row padding whenever Sk*esz is not
+    a multiple of 4. The padding holds NaN / +inf (fp forms) or stray keep bytes (bool), which
+    must not reach the output. Sq = 100 ends 32-row windows at rows 31, 63, 95 and 99."""
+    w = W.WORKLOADS["tiny"]
+    Sq, H = 100, 2
+    q, k, v = W.make_qkv(w, H=H, Sq=Sq, Sk=Sk)
+    rs = np.random.default_rng(Sk)
+    esz = {"fp32": 4, "bf16": 2, "fp16": 2, "bool": 1}[kind]
+    pad = -(-Sk * esz // 16) * 16 // esz
+    shape = (1, H, Sq, pad)
+    if kind == "bool":
+        full = rs.random(shape) < 0.02
+        full[..., Sk - 6:Sk] = True
+        full[..., Sk:] = rs.random((1, H, Sq, pad - Sk)) < 0.5
+        ref_b = np.where(full[..., :Sk], 0.0, -np.inf).astype(np.float32)
+        dev_b = torch.from_numpy(full).to(DEV)[..., :Sk]
+    else:
+        vals = rs.standard_normal(shape).astype(np.float32)
+        vals[..., Sk - 6:Sk] += 6.0
+        vals[..., Sk::2] = np.nan
+        vals[..., Sk + 1::2] = np.inf
+        full = {"fp32": vals, "bf16": W.f32_to_bf16_bits(vals), "fp16": vals.astype(np.float16)}[kind]
+        ref_b = full[..., :Sk]
+        dev_b = up(full)[..., :Sk]
+    ref = oracle.quantize_qk(q, k)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b)
+    o, l = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, bias=dev_b, return_lse=True)
+    what = f"{kind} Sk={Sk}"
+    check_o(o, o_ref, what=what)
+    check_lse(l, l_ref, what=what)
+
+
 def test_bias2d_full_size_sampled():
     """B1 H16 S4096 D128 with a materialised bf16 [1,1,4096,4096] bias, sampled rows."""
     w = W.WORKLOADS["dense4k"]
