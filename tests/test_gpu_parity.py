@@ -872,3 +872,41 @@ def test_graph_capture_replays_new_paths():
         torch.cuda.synchronize()
         for i, (t, e) in enumerate(zip(outs, eager)):
             assert torch.equal(t, e), f"replay {rep}: captured output {i} differs from the eager step"
+
+
+def test_offsets_past_2_31_elements():
+    """B1 H144 S131072 D128 bf16: every tensor holds 2.4e9 elements, so the last heads' element
+    offsets pass 2^31. Quantization of heads 0 and 143 is bit-exact against the oracle, and the
+    first and last query rows of those heads match it through a 1000-key segment at the end of
+    the keys (which keeps the walk short). Inputs: N(0,1) from a seeded torch generator on the
+    device, rounded to bf16; the oracle reads the same values copied back."""
+    B, H, S, D = 1, 144, 131072, 128
+    assert B * H * S * D > 2**31
+    free, _ = torch.cuda.mem_get_info(DEV)
+    if free < 40 * 2**30:
+        pytest.skip("needs 40 GiB of free device memory")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2**31 + 7)
+
+    def draw():
+        x = torch.randn((B, H, S, D), generator=gen, device=DEV, dtype=torch.float32)
+        y = x.to(torch.bfloat16)
+        del x
+        return y
+
+    q, k, v = draw(), draw(), draw()
+    g = qfa.quantize_qk(q, k)
+    sm = float(np.float32(D ** -0.5))
+    seg = [(S - 1000, 1000)]
+    o, lse = qfa.attn_fwd(g, v, sm, segments=seg, return_lse=True)
+    torch.cuda.synchronize()
+    rows = np.r_[0:32, S - 32:S]
+    for h in (0, H - 1):
+        qh, kh, vh = (down(t[:, h:h + 1]) for t in (q, k, v))
+        ref = oracle.quantize_qk(qh, kh)
+        assert_quant_equal({n: g[n][:, h:h + 1] for n in ("q8", "qs", "k8", "ks", "kmean", "qmu")}, ref)
+        o_ref, l_ref = oracle.attn(ref, vh, sm, segments=seg, rows=rows)
+        check_o(o[0, h], o_ref, rows, f"head {h}")
+        check_lse(lse[0, h], l_ref, rows, f"head {h}")
+    del q, k, v, g, o, lse
+    torch.cuda.empty_cache()
