@@ -910,3 +910,35 @@ def test_offsets_past_2_31_elements():
         check_lse(lse[0, h], l_ref, rows, f"head {h}")
     del q, k, v, g, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp16", "fp32", "bool"])
+@pytest.mark.parametrize("walk", ["full_461", "full_462", "full_463", "segs_odd", "segs_even"])
+def test_key_terms_last_key(kind, walk):
+    """Per-key bias / keep mask `[1,1,1,K]`: the last keys of each walked range decide the output
+    (biased +8, or the only keys kept besides a few), so a key term lost at the end of a copy
+    range shows. Ranges end at odd and even key counts, with and without key segments."""
+    w = W.WORKLOADS["tiny"]
+    Sk = {"full_461": 461, "full_462": 462, "full_463": 463}.get(walk, 463)
+    segs = {"segs_odd": [(5, 121), (200, 61)], "segs_even": [(4, 124), (201, 60)]}.get(walk)
+    q, k, v = W.make_qkv(w, H=2, Sq=96, Sk=Sk)
+    rs = np.random.default_rng(Sk + len(walk))
+    ends = [s0 + n - 1 for s0, n in segs] if segs else [Sk - 1]
+    if kind == "bool":
+        keep = rs.random(Sk) < 0.05
+        for e in ends:
+            keep[e - 2:e + 1] = True
+        ref_b = np.where(keep, 0.0, -np.inf).astype(np.float32).reshape(1, 1, 1, Sk)
+        dev_b = torch.from_numpy(keep.reshape(1, 1, 1, Sk)).to(DEV)
+    else:
+        vals = (rs.standard_normal(Sk) * 0.5).astype(np.float32)
+        for e in ends:
+            vals[e] += 8.0
+        full = {"fp32": vals, "bf16": W.f32_to_bf16_bits(vals), "fp16": vals.astype(np.float16)}[kind]
+        ref_b = full.reshape(1, 1, 1, Sk)
+        dev_b = up(ref_b)
+    ref = oracle.quantize_qk(q, k)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, segments=segs)
+    o, l = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, bias=dev_b, segments=segs, return_lse=True)
+    check_o(o, o_ref, what=f"{kind} {walk}")
+    check_lse(l, l_ref, what=f"{kind} {walk}")
