@@ -156,10 +156,12 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * v:        [B,Hkv,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
  *           v_sh, v_ss); base and row strides 16-byte aligned; v_ss below
  *           2^24 elements (else QFA_ERR_UNSUPPORTED). Keys are processed in
- *           tiles of 64: a key that is excluded (segment edge, block-sparse
- *           pad key, -inf bias) but shares a visited tile with an attended
- *           key still enters the PV product with weight zero, so its V row
- *           must be finite (0 * inf and 0 * NaN are NaN).
+ *           tiles of 64. V rows past the end of a segment, of block-sparse pad
+ *           keys and past Sk are never read into the product (they may hold
+ *           anything). Any other excluded key of a visited tile (before a
+ *           segment's start, or excluded by a keep mask, a -inf bias or the
+ *           causal diagonal) enters the PV product with weight zero, so its V
+ *           row must be finite (0 * inf and 0 * NaN are NaN).
  * sm_scale: softmax scale (typically D^-0.5).
  * bias:     nullable additive per-key bias of bias_dtype (QFA_FP32, QFA_BF16
  *           or QFA_FP16), element (b,h,j) at bias + b*bias_sb + h*bias_sh + j;

@@ -548,10 +548,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
 #pragma unroll
     for (int i = 0; i < KI_W; ++i) lds_copy<16>(lds_addr(&kbuf[stage][(wave + i * NW) * 1024]), k_src[i], d);
   };
-  auto copy_v = [&](int stage, int tile, int valid) __attribute__((always_inline)) {
+  // V rows past the tile's walked range (past a segment's end, pad keys of
+  // block-sparse tiles, rows past Sk) read zero: the range ends at row hi and
+  // an out-of-range lane of a copy writes zeros to LDS, so a non-finite V row
+  // of such a key never meets its zero weight in the PV product. (Rows before
+  // lo, where a segment starts inside the tile, are read.)
+  auto copy_v = [&](int stage, int tile, int hi, int valid) __attribute__((always_inline)) {
     if constexpr (DUMP) return;
     const int key0 = tile * BN;
-    const int rows = valid ? min(BN, a.Sk - key0) : 0;
+    const int rows = valid ? hi - key0 : 0;
     const v4u d = buf_desc32(vbase + (int64_t)key0 * v_row, rows > 0 ? (rows - 1) * v_row + 2 * D : 0);
 #pragma unroll
     for (int i = 0; i < VI_W; ++i) lds_copy<16>(lds_addr(&vbuf[stage][(wave + i * NW) * 1024]), v_src[i], d);
@@ -648,7 +653,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     copy_terms(0, t0, l0, h0, v0);
     copy_terms(1, t1, l1, h1, v1);
     copy_k(0, t0, v0);
-    copy_v(0, t0, v0);
+    copy_v(0, t0, h0, v0);
     copy_k(1, t1, v1);
     wait_vmcnt<0>();
     // the keep-mask bytes wave 0 folds in were copied by wave 1
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
     next_tile(t2, l2, h2, v2);
     if constexpr (NSTG == 3) {
       copy_k(2, t2, v2);
-      copy_v(1, t1, v1);
+      copy_v(1, t1, h1, v1);
     }
   }
 
@@ -789,8 +794,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qt
         else copy_k(st0, t2, v2);                       // K(iter+2) over K(iter)
       }
     }
-    if constexpr (NSTG == 3) copy_v(st2, t2, v2);      // V(iter+2) over V(iter-1)
-    else copy_v(st1, t1, v1);                          // V(iter+1) over V(iter-1)
+    if constexpr (NSTG == 3) copy_v(st2, t2, h2, v2);       // V(iter+2) over V(iter-1)
+    else copy_v(st1, t1, h1, v1);                           // V(iter+1) over V(iter-1)
     if constexpr (BIAS2D) {
       // keys past Sk (only in the tile that holds key Sk - 1) read row
       // padding or the next row: excluded by their key terms, but a NaN or

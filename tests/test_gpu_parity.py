@@ -942,3 +942,50 @@ def test_key_terms_last_key(kind, walk):
     o, l = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, bias=dev_b, segments=segs, return_lse=True)
     check_o(o, o_ref, what=f"{kind} {walk}")
     check_lse(l, l_ref, what=f"{kind} {walk}")
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_nan_rows_past_walked_ranges_never_read(splits):
+    """NaN in V after a segment's end inside a visited tile (keys 100..127 and 227..299 for
+    segments (0,100), (150,77); keys 128..149 before the second segment's start stay finite,
+    as the header requires) leaves the output equal to the oracle's, which never reads them."""
+    w = W.WORKLOADS["tiny"]
+    Sk = 300
+    q, k, v = W.make_qkv(w, H=2, Sq=130, Sk=Sk)
+    segs = [(0, 100), (150, 77)]
+    ref = oracle.quantize_qk(q, k)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, segments=segs)
+    vn = v.copy()
+    nan_bits = np.uint16(0x7FC0)   # bf16 quiet NaN
+    vn[:, :, 100:128, :] = nan_bits
+    vn[:, :, 227:, :] = nan_bits
+    o, l = qfa.attn_fwd(gpu_quant(q, k), up(vn), w.sm_scale, segments=segs, splits=splits, return_lse=True)
+    check_o(o, o_ref, what=f"segments, splits {splits}")
+    check_lse(l, l_ref, what=f"segments, splits {splits}")
+
+
+def test_nan_pad_rows_block_sparse():
+    """Block-sparse: NaN in the pad rows (j mod 64 >= vbs) of Q, K and V; quantization gives
+    their codes 0 / scale 0 and leaves them out of the K mean, and the V copies stop at vbs, so
+    the output equals the oracle's on the same inputs with zero pad rows."""
+    w = W.WORKLOADS["sparse"]
+    S, H = 512, 2
+    T = S // 64
+    q, k, v = W.make_qkv(w, H=H, Sq=S, Sk=S)
+    vbs = np.array([64, 17, 0, 40, 64, 1, 63, 17], np.int32)
+    for x in (q, k, v):
+        W.zero_pads(x, vbs)
+    mask = np.random.default_rng(5).random((1, H, T, T)) < 0.7
+    ref = oracle.quantize_qk(q, k, vbs)
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, mask=mask.astype(np.uint8), vbs=vbs)
+    j = np.arange(S)
+    pad = (j % 64) >= vbs[j // 64]
+    qn, kn, vn = q.copy(), k.copy(), v.copy()
+    for x in (qn, kn, vn):
+        x[:, :, pad, :] = np.uint16(0x7FC0)
+    g = qfa.quantize_qk(up(qn), up(kn), up(vbs))
+    idx, cnt = qfa.blockmask_to_index(up(mask))
+    o, l = qfa.attn_fwd(g, up(vn), w.sm_scale, index=idx, count=cnt, vbs=up(vbs), return_lse=True)
+    valid_rows = np.flatnonzero(~np.tile(pad, H))
+    check_o(o, o_ref[valid_rows], valid_rows, "sparse pads NaN")
+    check_lse(l, l_ref[valid_rows], valid_rows, "sparse pads NaN")
