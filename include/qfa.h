@@ -48,7 +48,7 @@ extern "C" {
 /* Status codes. */
 #define QFA_OK 0
 #define QFA_ERR_INVALID_ARG 1 /* a null/misaligned pointer, bad size, stride or combination */
-#define QFA_ERR_UNSUPPORTED 2 /* valid request this build does not implement (e.g. D not in {64,128}) */
+#define QFA_ERR_UNSUPPORTED 2 /* valid request the library does not implement (e.g. D not in {64,128}) */
 #define QFA_ERR_HIP 3         /* the HIP runtime rejected a launch */
 
 /* Element types. */

@@ -52,7 +52,7 @@ int check_dims(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
   if (D != 64 && D != 128) return fail(QFA_ERR_UNSUPPORTED, "head dimension %lld (supported: 64, 128)", (long long)D);
   if (B * H > (1ll << 24) || Sq > (1ll << 30) || Sk > (1ll << 30))
-    return fail(QFA_ERR_UNSUPPORTED, "sizes beyond this build's 32-bit tile indexing");
+    return fail(QFA_ERR_UNSUPPORTED, "sizes beyond the kernels' 32-bit tile indexing");
   return QFA_OK;
 }
 
