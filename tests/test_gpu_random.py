@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import quantized_flash_attention_amd as qfa
 
-N_CONFIGS = 32
+N_CONFIGS = 96
 
 
 def _config(i):
