@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import DEV, check_lse, check_o, up
+from tests.gpu_util import DEV, check_lse, check_o, sample_rows, up
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,58 @@ def test_random_config(i):
     check_o(o, o_ref, what=what)
     if c["lse"]:
         check_lse(res[1], l_ref, what=what)
+
+
+N_LARGE = 12
+
+
+def _large_config(i):
+    """Large shapes: many query blocks per head, long key walks (split-K ranges over hundreds of
+    tiles), causal orders over several CU rounds; rows are sampled."""
+    rs = np.random.default_rng(5000 + i)
+    wn = ["dense4k", "d64", "band"][rs.integers(3)]
+    Hkv = int(rs.integers(1, 5))
+    H = Hkv * int(rs.integers(1, 3))
+    B = int(rs.integers(1, 3))
+    unquant = bool(rs.random() < 0.25)
+    Sq = int(rs.integers(1, 4500))
+    Sk = Sq if rs.random() < 0.4 else int(rs.integers(1, 40000))
+    causal = Sq == Sk and bool(rs.random() < 0.6)
+    segments = None
+    if not causal and rs.random() < 0.4 and Sk > 8:
+        cuts = np.sort(rs.choice(np.arange(Sk + 1), size=4, replace=False))
+        segments = [(int(cuts[0]), int(cuts[1] - cuts[0])), (int(cuts[2]), int(cuts[3] - cuts[2]))]
+    kinds = ["none", "key_fp32", "key_bf16", "key_bool"] + ([] if unquant else ["query_bf16", "query_bool"])
+    bias = kinds[rs.integers(len(kinds))]
+    if bias.startswith("query") and B * H * Sq * Sk > 3e7:
+        bias = "key_bf16"   # keep the host-side draw of a materialised bias to seconds
+    return dict(w=wn, B=B, H=H, Hkv=Hkv, Sq=Sq, Sk=Sk, unquant=unquant, causal=causal, segments=segments,
+                bias=bias, vscale=bool(rs.random() < 0.3), splits=["auto", 1, 2, 5][rs.integers(4)],
+                lse=bool(rs.random() < 0.7), seed=5000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_config(i):
+    c = _large_config(i)
+    w = W.WORKLOADS[c["w"]]
+    rs = np.random.default_rng(c["seed"])
+    B, H, Sq, Sk, Hkv = c["B"], c["H"], c["Sq"], c["Sk"], c["Hkv"]
+    q, k, v = W.make_qkv(w, B=B, H=H, Hkv=Hkv, Sq=Sq, Sk=Sk)
+    bias_ref, bias_dev = _bias(c["bias"], B, H, Sq, Sk, rs)
+    vsc = W.v_scale(w, H=Hkv) if c["vscale"] else None
+    rows = sample_rows(B, H, Sq, per_head=48, heads=sorted({0, H - 1}), seed=c["seed"])
+    kw_o = dict(bias=bias_ref, v_scale=vsc, segments=c["segments"], causal=c["causal"], rows=rows)
+    kw_g = dict(bias=bias_dev, v_scale=None if vsc is None else up(vsc), segments=c["segments"],
+                causal=c["causal"], splits=c["splits"], return_lse=c["lse"])
+    if c["unquant"]:
+        o_ref, l_ref = oracle.attn(None, v, w.sm_scale, q=W.to_f32(q), k=W.to_f32(k), **kw_o)
+        res = qfa.attn_fwd_unquant(up(q), up(k), up(v), w.sm_scale, **kw_g)
+    else:
+        ref = oracle.quantize_qk(q, k)
+        o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, **kw_o)
+        res = qfa.attn_fwd(qfa.quantize_qk(up(q), up(k)), up(v), w.sm_scale, **kw_g)
+    o = res[0] if c["lse"] else res
+    what = f"large config {i}: {c}"
+    check_o(o, o_ref, rows, what)
+    if c["lse"]:
+        check_lse(res[1], l_ref, rows, what)
