@@ -657,19 +657,33 @@ def test_merge_neg_inf_partials():
 
 # ------------------------------------------------------------ block-sparse --
 
-def test_blockmask_to_index_exact():
-    rs = np.random.default_rng(21)
-    mask = rs.random((2, 3, 37, 200)) < 0.2
+@pytest.mark.parametrize("Tk,aligned", [(200, True), (1, True), (17, True), (16, True), (32, True),
+                                         (1024, True), (1040, True), (2048, True), (32, False)])
+@pytest.mark.parametrize("density", [0.0, 0.02, 0.5, 1.0])
+def test_blockmask_to_index_exact(Tk, aligned, density):
+    """Counts and ascending lists bit-exact against the oracle. Rows of a multiple of 16 bytes on an
+    aligned base take the 16-bytes-per-lane kernel (1040: a partial 1024-byte step), the others
+    (and a base one byte off) the byte-per-lane one."""
+    rs = np.random.default_rng(21 + Tk)
+    shape = (2, 3, 37, Tk)
+    mask = rs.random(shape) < density
     mask[0, 0, 0] = False
     mask[1, 2, 3] = True
-    idx, cnt = qfa.blockmask_to_index(up(mask))
+    if aligned:
+        dev = up(mask)
+    else:
+        flat = torch.zeros(mask.size + 1, dtype=torch.bool, device=DEV)
+        flat[1:] = up(mask.reshape(-1))
+        dev = flat[1:].view(shape)
+        assert dev.data_ptr() % 16 == 1
+    idx, cnt = qfa.blockmask_to_index(dev)
     r_idx, r_cnt = oracle.blockmask_to_index(mask)
     cnt = cnt.cpu().numpy()
     idx = idx.cpu().numpy()
     assert np.array_equal(cnt, r_cnt)
-    for b, h, t in np.ndindex(2, 3, 37):
+    for b, h, t in np.ndindex(*shape[:3]):
         n = r_cnt[b, h, t]
-        assert np.array_equal(idx[b, h, t, :n], r_idx[b, h, t, :n])
+        assert np.array_equal(idx[b, h, t, :n], r_idx[b, h, t, :n]), (b, h, t)
 
 
 def _sparse_case(T, H, mask, vbs, rows=None, Hkv=None):
