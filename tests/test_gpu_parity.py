@@ -847,6 +847,48 @@ def test_graph_capture_replays():
             assert torch.equal(t, e), f"replay {rep}: a captured output differs from the eager step"
 
 
+def test_graph_capture_replays_block_sparse():
+    """The block-sparse path (tile mask to index lists, quantize with vbs, sparse attention with a
+    V scale and LSE) captured in one HIP graph: every replay, with eager work and synchronisation
+    between replays, reproduces the eager results bit for bit."""
+    w = W.WORKLOADS["sparse"]
+    T, H = 32, 2
+    S = 64 * T
+    q, k, v = W.make_qkv(w, H=H, Sq=S, Sk=S)
+    vbs = W.sparse_vbs(T)
+    for x in (q, k, v):
+        W.zero_pads(x, vbs)
+    mask = W.sparse_mask(T, H, prefix=2, band=4)
+    tq, tk, tv, tm, tvbs = up(q), up(k), up(v), up(mask), up(vbs)
+    tvs = up(W.v_scale(w, H=H))
+
+    def step():
+        idx, cnt = qfa.blockmask_to_index(tm)
+        qk = qfa.quantize_qk(tq, tk, tvbs)
+        o, l = qfa.attn_fwd(qk, tv, w.sm_scale, index=idx, count=cnt, vbs=tvbs, v_scale=tvs, return_lse=True)
+        return [cnt, qk["q8"], qk["k8"], qk["qs"], qk["ks"], o, l]
+
+    eager = [t.clone() for t in step()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(outs, eager):
+            assert torch.equal(t, e), f"replay {rep}: a captured output differs from the eager step"
+
+
 def test_graph_capture_replays_new_paths():
     """Split-K (partials + combine), causal with GQA, the unquantized-QK path and a
     materialised per-query keep mask, captured in one HIP graph with caller-provided
