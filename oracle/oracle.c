@@ -36,8 +36,9 @@
  *
  * Readings where the pages leave a step open (each is also a test):
  *  R1 the K mean is the exact sum over valid keys, rounded once to fp64,
- *     divided by n in fp64 and rounded to fp32; n = Sk, or max(1, sum vbs)
- *     when a validity vector is given.  The exact sum is accumulated in
+ *     divided by n in fp64 and rounded to fp32; n = max(1, Sk), or
+ *     max(1, sum vbs) when a validity vector is given (the pages clamp the
+ *     valid count to 1; the same clamp gives an empty K the mean 0).  The exact sum is accumulated in
  *     __float128, which is exact for bf16/fp16 data whose bit span stays
  *     below 113 bits (always for fp16; bf16 within a 2^+-40 magnitude band).
  *  R2 quantizer: a = max|x|; rows with a < 127*FLT_MIN (the scale would be
@@ -107,8 +108,8 @@ void oracle_kmean(const void* k, int dtype, int64_t B, int64_t H, int64_t S, int
     if (vbs) {
         n = 0;
         for (int64_t t = 0; t < (S + 63) / 64; ++t) n += vbs[t];
-        if (n < 1) n = 1;
     }
+    if (n < 1) n = 1;   /* reading R1: the count is clamped to 1, so an empty K has mean 0 */
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t bh = 0; bh < B * H; ++bh)
         for (int64_t c = 0; c < D; ++c) {

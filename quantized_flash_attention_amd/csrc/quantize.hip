@@ -222,6 +222,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a, int
 
 hipError_t launch_kmean(const MeanArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nchunks * a.B * a.H);
+  if (grid == 0) return hipSuccess;   // no (b,h) pair or no rows: nothing to average
   if (a.D == 128) {
     if (a.dtype == BF16) kmean_partial_kernel<BF16, 128><<<grid, 256, 0, s>>>(a);
     else kmean_partial_kernel<FP16, 128><<<grid, 256, 0, s>>>(a);

@@ -227,6 +227,27 @@ def test_attn_edge_cases():
     assert out.shape[2] == 0
 
 
+@pytest.mark.parametrize("center", [True, False])
+def test_empty_shapes(center):
+    """Empty batch, no heads and no keys are valid calls: nothing to do for B = 0 or H = 0; with
+    Sk = 0 the K mean is 0 (the count is clamped to 1), every row has nothing to attend (O = 0,
+    LSE = -inf), and the centring term is 0."""
+    for B, H, Sq, Sk in ((0, 2, 64, 64), (1, 0, 64, 64), (1, 2, 64, 0), (2, 2, 0, 0)):
+        q = torch.zeros((B, H, Sq, 128), dtype=torch.bfloat16, device=DEV).normal_()
+        k = torch.zeros((B, H, Sk, 128), dtype=torch.bfloat16, device=DEV).normal_()
+        v = torch.zeros((B, H, Sk, 128), dtype=torch.bfloat16, device=DEV).normal_()
+        g = qfa.quantize_qk(q, k, center_k=center)
+        o, l = qfa.attn_fwd(g, v, 128 ** -0.5, return_lse=True)
+        torch.cuda.synchronize()
+        assert o.shape == (B, H, Sq, 128) and l.shape == (B, H, Sq)
+        if center:
+            assert torch.all(g["kmean"] == 0) or Sk > 0
+        if Sk == 0 and B * H * Sq > 0:
+            assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+            if center:
+                assert torch.all(g["qmu"] == 0)
+
+
 def test_keep_mask():
     """A bool [1,1,1,K] keep mask (True attends) equals the additive bias 0 / -inf: the banded
     weights thresholded at 1e-3, a random mask over key segments, and an all-false mask (every

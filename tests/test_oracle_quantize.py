@@ -146,3 +146,16 @@ def test_scores_i32_brute_force(oracle_lib):
     big[1] = -127
     s2 = oracle_lib.scores_i32(big, big)
     assert s2.tolist() == [[128 * 127 * 127, -128 * 127 * 127], [-128 * 127 * 127, 128 * 127 * 127]]
+
+
+def test_kmean_of_no_keys_is_zero(oracle_lib):
+    """Reading R1: the count is clamped to 1, so an empty K (dense or all-pad) has mean 0 and the
+    centring term of every query row is 0."""
+    k = np.zeros((2, 3, 0, 128), np.uint16)
+    assert np.array_equal(oracle_lib.kmean(k), np.zeros((2, 3, 128), np.float32))
+    q = W.normal(1, 0, (2, 3, 5, 128), "bf16")
+    ref = oracle_lib.quantize_qk(q, k)
+    assert np.array_equal(ref["kmean"], np.zeros((2, 3, 128), np.float32))
+    assert np.array_equal(ref["qmu"], np.zeros((2, 3, 5)))
+    kp = W.normal(1, 1, (1, 1, 64, 128), "bf16")
+    assert np.array_equal(oracle_lib.kmean(kp, np.array([0], np.int32)), np.zeros((1, 1, 128), np.float32))
