@@ -91,6 +91,13 @@ int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, si
  * n = Sk, or max(1, sum(vbs)) when vbs is given; K - mu is one fp32
  * subtraction. qmu[b,h,i] = sum_c Q[b,h,i,c]*mu[b,h/(H/Hkv),c] (fp32) lets
  * attn_fwd report the LSE of the uncentred scores.
+ * Non-finite values (the pages do not treat them; this library's reading):
+ * a row of Q, or of K - mu, holding a NaN or +-inf gets codes 0 and scale
+ * NaN, and for Q a NaN qmu; a K channel whose valid keys hold a NaN or
+ * +-inf gets a NaN mean, so every centred K row of that K/V head is such a
+ * row. Pad rows (vbs) are never read. Scores involving a NaN scale are NaN,
+ * and qfa_attn_fwd's output for a query row that attends such a score is
+ * unspecified (no fault).
  *
  * H, Hkv:  heads of Q and of K. Hkv divides H; Hkv < H is grouped-query
  *          attention (ROCm/FlyDSL PR #886 tests and times "MHA and GQA"):
@@ -150,8 +157,11 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  * H, Hkv:  heads of Q and of K/V; Hkv divides H, and query head h reads K/V
  *           head h / (H/Hkv) (grouped-query attention when Hkv < H).
  * q8, qs:   int8 [B,H,Sq,D], fp32 [B,H,Sq] (from qfa_quantize_qk).
- * qmu:      nullable fp32 [B,H,Sq]; when given, sm_scale*qmu is added to the
- *           LSE (pass it whenever K was centred and the LSE is requested).
+ * qmu:      nullable fp32 [B,H,Sq]; sm_scale*qmu is added to the LSE.
+ * k_centered: nonzero when k8/ks were quantized from K - mu (center_k of
+ *           qfa_quantize_qk). The LSE is then only right with the centring
+ *           term, so lse != NULL with k_centered and qmu == NULL is rejected
+ *           (QFA_ERR_INVALID_ARG), as is qmu != NULL without k_centered.
  * k8, ks:   int8 [B,Hkv,Sk,D], fp32 [B,Hkv,Sk].
  * v:        [B,Hkv,Sk,D] of v_dtype (QFA_BF16 or QFA_FP16), strides (v_sb,
  *           v_sh, v_ss); base and row strides 16-byte aligned; v_ss below
@@ -208,7 +218,7 @@ int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq
  */
 int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                  const int8_t* q8, const float* qs, const float* qmu,
-                 const int8_t* k8, const float* ks,
+                 const int8_t* k8, const float* ks, int k_centered,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                  float sm_scale,
                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
@@ -259,7 +269,7 @@ int qfa_qk_scores_i32(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
  */
 int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                         const int8_t* q8, const float* qs, const float* qmu,
-                        const int8_t* k8, const float* ks,
+                        const int8_t* k8, const float* ks, int k_centered,
                         const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                         float sm_scale,
                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,

@@ -6,8 +6,9 @@ library never imports, links or runs anything under ``oracle/``.
 
 This module is argument marshalling around ``oracle.c`` (plain C, fp64 from
 the logits on; see the header of that file for the steps, the sources they
-follow and the readings taken where the pages are silent) plus ``exact.py``,
-textbook fp64 attention without quantization.
+follow and the readings taken where the pages are silent). Its no-quant mode
+(``attn`` with ``q``/``k`` instead of codes) is textbook fp64 attention; the
+tests pin it against torch's fp64 scaled_dot_product_attention and logsumexp.
 
 Array conventions: numpy arrays, C-contiguous after ``np.ascontiguousarray``.
 bf16 tensors are carried as ``np.uint16`` arrays holding the raw bf16 bits;

@@ -55,6 +55,11 @@
  *     multiple of Hkv), query head h reading K/V head h / (H/Hkv) (runs of
  *     consecutive query heads per K/V head); K mean, K codes and the V scale
  *     belong to the K/V head, and q.mu of a query row uses its K/V head's mean.
+ *  R9 non-finite inputs: a row of Q or of K - mu holding a NaN or +-inf
+ *     quantizes to codes 0 with scale NaN (its centring term is NaN too),
+ *     and a K channel whose valid keys hold a NaN or +-inf has mean NaN, so
+ *     every centred K row of that head is such a row. Scores with such a
+ *     row are NaN.
  *
  * Parity pins (tests/test_oracle_*.py): hand-worked quantization examples
  * (tests/golden/), exact-rational means, brute-force integer scores, the
@@ -114,12 +119,15 @@ void oracle_kmean(const void* k, int dtype, int64_t B, int64_t H, int64_t S, int
     for (int64_t bh = 0; bh < B * H; ++bh)
         for (int64_t c = 0; c < D; ++c) {
             __float128 acc = 0;
+            int finite = 1;
             for (int64_t j = 0; j < S; ++j) {
                 if (is_pad_row(vbs, j)) continue;
-                acc += (__float128)load_elem(k, dtype, (bh * S + j) * D + c);
+                float x = load_elem(k, dtype, (bh * S + j) * D + c);
+                if (!isfinite(x)) finite = 0;             /* reading R9 */
+                acc += (__float128)x;
             }
             double sum = (double)acc;                 /* exact sum rounded once */
-            mean[bh * D + c] = (float)(sum / (double)n);
+            mean[bh * D + c] = finite ? (float)(sum / (double)n) : NAN;
         }
 }
 
@@ -128,6 +136,11 @@ void oracle_kmean(const void* k, int dtype, int64_t B, int64_t H, int64_t S, int
 static void quantize_one_row(const float* x, int64_t D, int8_t* q, float* scale) {
     float a = 0.0f;
     for (int64_t c = 0; c < D; ++c) {
+        if (!isfinite(x[c])) {                           /* reading R9 */
+            for (int64_t d = 0; d < D; ++d) q[d] = 0;
+            *scale = NAN;
+            return;
+        }
         float m = fabsf(x[c]);
         if (m > a) a = m;
     }
@@ -181,8 +194,11 @@ void oracle_qmu(const void* qx, int dtype, int64_t B, int64_t H, int64_t Hkv, in
         int64_t kvh = (bh / H) * Hkv + (bh % H) / (H / Hkv);
         double acc = 0.0;
         if (!is_pad_row(vbs, j))
-            for (int64_t c = 0; c < D; ++c)
-                acc += (double)load_elem(qx, dtype, r * D + c) * (double)mean[kvh * D + c];
+            for (int64_t c = 0; c < D; ++c) {
+                float x = load_elem(qx, dtype, r * D + c);
+                if (!isfinite(x)) { acc = NAN; break; }    /* reading R9 */
+                acc += (double)x * (double)mean[kvh * D + c];
+            }
         qmu[r] = acc;
     }
 }

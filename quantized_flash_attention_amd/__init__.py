@@ -233,7 +233,9 @@ def attn_fwd(qk: dict, v: torch.Tensor, sm_scale: float | None = None, *, bias: 
     _shape(qmu, "qmu", (B, H, Sq))
     _cont(q8, "q8", torch.int8), _cont(k8, "k8", torch.int8)
     _cont(qs, "qs", torch.float32), _cont(ks, "ks", torch.float32), _cont(qmu, "qmu", torch.float32)
-    qk_args = (_ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks))
+    # codes of centred K carry their mean; without it the caller states the K was not centred
+    centered = qk.get("kmean") is not None
+    qk_args = (_ptr(q8), _ptr(qs), _ptr(qmu), _ptr(k8), _ptr(ks), int(centered))
     return _attn_call(B, H, Hkv, Sq, Sk, D, qk_args, False, v, sm_scale, bias, index, count, vbs, v_scale, segments,
                       causal, out, out_dtype, return_lse, lse, splits, workspace)
 

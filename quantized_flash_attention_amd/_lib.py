@@ -56,14 +56,18 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_quantize_qk.restype = _I
     L.qfa_blockmask_to_index.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.qfa_blockmask_to_index.restype = _I
-    L.qfa_attn_fwd.argtypes = ([_I64] * 6 + [_P] * 5 + [_P, _I, _I64, _I64, _I64] + [ctypes.c_float]
-                               + [_P, _I, _I64, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
-                               + [_P, _I, _I64, _I64, _I64] + [_P, _P])
+    # sm_scale, bias, block-sparse lists, v_scale, segments, causal, out, lse
+    masks_out = ([ctypes.c_float] + [_P, _I, _I64, _I64, _I64] + [_P] * 3 + [_P, _I, _P, _I]
+                 + [_P, _I, _I64, _I64, _I64] + [_P])
+    v_view = [_P, _I, _I64, _I64, _I64]
+    # q8, qs, qmu, k8, ks, k_centered
+    codes = [_P] * 5 + [_I]
+    L.qfa_attn_fwd.argtypes = [_I64] * 6 + codes + v_view + masks_out + [_P]
     L.qfa_attn_fwd.restype = _I
-    L.qfa_attn_fwd_splitk.argtypes = L.qfa_attn_fwd.argtypes[:-1] + [_I, _P, ctypes.c_size_t, _P]
+    L.qfa_attn_fwd_splitk.argtypes = [_I64] * 6 + codes + v_view + masks_out + [_I, _P, ctypes.c_size_t, _P]
     L.qfa_attn_fwd_splitk.restype = _I
-    L.qfa_attn_fwd_unquant.argtypes = ([_I64] * 6 + [_P, _I64, _I64, _I64] * 2 + [_P, _I, _I64, _I64, _I64]
-                                       + L.qfa_attn_fwd.argtypes[16:-1] + [_I, _P, ctypes.c_size_t, _P])
+    L.qfa_attn_fwd_unquant.argtypes = ([_I64] * 6 + [_P, _I64, _I64, _I64] * 2 + v_view + masks_out
+                                       + [_I, _P, ctypes.c_size_t, _P])
     L.qfa_attn_fwd_unquant.restype = _I
     L.qfa_attn_split_workspace_bytes.argtypes = [_I64] * 4 + [_I, ctypes.POINTER(ctypes.c_size_t)]
     L.qfa_attn_split_workspace_bytes.restype = _I

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "qfa_internal.h"
@@ -73,9 +74,31 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace qfa {
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("QFA_DEBUG");
+    return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void debug_log(const char* fmt, ...) {
+  if (!debug_enabled()) return;
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "qfa: %s\n", line);
+}
+
+}  // namespace qfa
+
 extern "C" {
 
-int qfa_version(void) { return 300; }
+int qfa_version(void) { return 400; }
 
 const char* qfa_status_string(int status) {
   switch (status) {
@@ -92,17 +115,22 @@ const char* qfa_last_error(void) { return g_err; }
 int qfa_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Sk, int64_t D, size_t* bytes) {
   if (!bytes) return fail(QFA_ERR_INVALID_ARG, "bytes is NULL");
   if (B < 0 || H < 0 || Sk < 0 || D <= 0) return fail(QFA_ERR_INVALID_ARG, "negative size");
-  const int64_t nchunks = (Sk + qfa::kMeanChunkRows - 1) / qfa::kMeanChunkRows;
-  *bytes = (size_t)(B * H * nchunks * D) * 16;
+  *bytes = (size_t)qfa::quantize_workspace_size(B * H, Sk, D);
   return ok();
 }
 
-int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
-                    const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
-                    const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
-                    const int32_t* vbs, int center_k,
-                    int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks and launches of qfa_quantize_qk, on a workspace the caller (or the
+// allocation-free entry point) provides.
+int quantize_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                  const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                  const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                  const int32_t* vbs, int center_k,
+                  int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   int st;
   if ((st = check_dims(B, H, Sq, Sk, D))) return st;
   if ((st = check_kv_heads(H, Hkv))) return st;
@@ -126,30 +154,36 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, i
   if (center_k) {
     if (!kmean) return fail(QFA_ERR_INVALID_ARG, "kmean output is NULL with center_k");
     if (!aligned16(kmean) || (qmu && !aligned16(qmu))) return fail(QFA_ERR_INVALID_ARG, "kmean/qmu must be 16-byte aligned");
-    size_t need = 0;
-    qfa_quantize_workspace_bytes(B, Hkv, Sk, D, &need);
+    const size_t need = (size_t)qfa::quantize_workspace_size(B * Hkv, Sk, D);
     if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-      return fail(QFA_ERR_INVALID_ARG, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+      return fail(QFA_ERR_INVALID_ARG, "workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
   }
-  hipStream_t s = (hipStream_t)stream;
-  if (center_k && Sk > 0) {
-    qfa::MeanArgs m{k, dtype, B, Hkv, Sk, D, k_sb, k_sh, k_ss, vbs, (double2*)workspace, kmean,
-                    (int)((Sk + qfa::kMeanChunkRows - 1) / qfa::kMeanChunkRows)};
-    if ((st = hip_status(qfa::launch_kmean(m, s), "kmean launch"))) return st;
-  } else if (center_k) {
-    if ((st = hip_status(qfa::launch_zero_words(kmean, B * Hkv * D, s), "kmean clear"))) return st;
-  }
-  if (Sq > 0) {
-    qfa::QuantRowsArgs qa{q, dtype, B, H, Sq, D, q_sb, q_sh, q_ss, nullptr,
-                          center_k ? kmean : nullptr, Hkv, vbs, q8, qs, center_k ? qmu : nullptr};
-    if ((st = hip_status(qfa::launch_quantize_rows(qa, s), "quantize Q launch"))) return st;
-  }
-  if (Sk > 0) {
-    qfa::QuantRowsArgs ka{k, dtype, B, Hkv, Sk, D, k_sb, k_sh, k_ss, center_k ? kmean : nullptr,
-                          nullptr, Hkv, vbs, k8, ks, nullptr};
-    if ((st = hip_status(qfa::launch_quantize_rows(ka, s), "quantize K launch"))) return st;
-  }
-  return ok();
+  qfa::QuantArgs a{};
+  a.dtype = dtype;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.D = D;
+  a.q = q; a.q_sb = q_sb; a.q_sh = q_sh; a.q_ss = q_ss;
+  a.k = k; a.k_sb = k_sb; a.k_sh = k_sh; a.k_ss = k_ss;
+  a.vbs = vbs;
+  a.q8 = q8; a.qs = qs; a.qmu = center_k ? qmu : nullptr;
+  a.k8 = k8; a.ks = ks;
+  a.kmean = center_k ? kmean : nullptr;
+  a.workspace = workspace;
+  return hip_status(qfa::launch_quantize(a, (hipStream_t)stream), "quantize launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                    const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                    const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                    const int32_t* vbs, int center_k,
+                    int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_impl(B, H, Hkv, Sq, Sk, D, dtype, q, q_sb, q_sh, q_ss, k, k_sb, k_sh, k_ss, vbs, center_k,
+                       q8, qs, k8, ks, kmean, qmu, workspace, workspace_bytes, stream);
 }
 
 int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
@@ -210,6 +244,7 @@ struct QKSrc {
   const float* qmu;
   const int8_t* k8;
   const float* ks;
+  int k_centered;       // k8/ks come from K - mu
   const void* qf;
   const void* kf;
   int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss;
@@ -235,6 +270,10 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
   } else {
     if (!qk.q8 || !qk.qs) return fail(QFA_ERR_INVALID_ARG, "q8/qs is NULL");
     if (!aligned16(qk.q8)) return fail(QFA_ERR_INVALID_ARG, "q8 must be 16-byte aligned");
+    // the LSE of centred codes needs the centring term sm_scale * q.mu
+    if (lse && qk.k_centered && !qk.qmu)
+      return fail(QFA_ERR_INVALID_ARG, "LSE requested on centred K codes without qmu (the centring term)");
+    if (qk.qmu && !qk.k_centered) return fail(QFA_ERR_INVALID_ARG, "qmu given but K is not centred");
   }
   if (Sk > 0) {  // with no keys every row is fully masked and K/V are never read
     if (unquant) {
@@ -343,7 +382,7 @@ int attn_fwd_impl(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int
 
 int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                  const int8_t* q8, const float* qs, const float* qmu,
-                 const int8_t* k8, const float* ks,
+                 const int8_t* k8, const float* ks, int k_centered,
                  const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                  float sm_scale,
                  const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
@@ -351,7 +390,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
                  const float* v_scale, int nseg, const int64_t* seg, int causal,
                  void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                  float* lse, void* stream) {
-  const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  const QKSrc qk{q8, qs, qmu, k8, ks, k_centered, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
                        bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, 1, nullptr, 0, stream);
@@ -359,7 +398,7 @@ int qfa_attn_fwd(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int6
 
 int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                         const int8_t* q8, const float* qs, const float* qmu,
-                        const int8_t* k8, const float* ks,
+                        const int8_t* k8, const float* ks, int k_centered,
                         const void* v, int v_dtype, int64_t v_sb, int64_t v_sh, int64_t v_ss,
                         float sm_scale,
                         const void* bias, int bias_dtype, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
@@ -367,7 +406,7 @@ int qfa_attn_fwd_splitk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t S
                         const float* v_scale, int nseg, const int64_t* seg, int causal,
                         void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                         float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  const QKSrc qk{q8, qs, qmu, k8, ks, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  const QKSrc qk{q8, qs, qmu, k8, ks, k_centered, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, v_dtype, v_sb, v_sh, v_ss, sm_scale,
                        bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,
                        out, out_dtype, o_sb, o_sh, o_ss, lse, num_splits, workspace, workspace_bytes, stream);
@@ -383,7 +422,7 @@ int qfa_attn_fwd_unquant(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t 
                          const float* v_scale, int nseg, const int64_t* seg, int causal,
                          void* out, int out_dtype, int64_t o_sb, int64_t o_sh, int64_t o_ss,
                          float* lse, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  const QKSrc qk{nullptr, nullptr, nullptr, nullptr, nullptr, q, k, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  const QKSrc qk{nullptr, nullptr, nullptr, nullptr, nullptr, 0, q, k, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   if (!q && B * H * Sq > 0) return fail(QFA_ERR_INVALID_ARG, "q is NULL");
   return attn_fwd_impl(B, H, Hkv, Sq, Sk, D, qk, v, dtype, v_sb, v_sh, v_ss, sm_scale,
                        bias, bias_dtype, bias_sb, bias_sh, bias_sq, index, count, vbs, v_scale, nseg, seg, causal,

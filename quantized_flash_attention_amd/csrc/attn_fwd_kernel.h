@@ -975,6 +975,16 @@ hipError_t launch_d_vt(const AttnArgs& a, hipStream_t s) {
   // split partials always carry their LSE
   const bool lse = a.lse != nullptr || ns > 1;
   constexpr bool F = false, T = true;
+  if (debug_enabled()) {
+    const bool bias2d = !QB && !sparse && a.bias && a.bias_sq != 0;
+    const bool keyterm_bias = !sparse && !bias2d && a.bias && a.bias_dtype != BOOL;
+    const bool keep = !sparse && !bias2d && a.bias && a.bias_dtype == BOOL;
+    debug_log("attn_fwd_kernel<D=%d, V=%s, sparse=%d, bias=%d, lse=%d, causal=%d, qk=%s, bias2d=%d> keep_mask=%d "
+              "grid %d x 256 (query blocks %d, B*H %d, splits %d) Sq %d Sk %d segments %d out %s",
+              D, VT == BF16 ? "bf16" : "fp16", (int)sparse, (int)keyterm_bias, (int)lse, a.causal, QB ? "bf16/fp16" : "int8",
+              (int)bias2d, (int)keep, total, qtiles, a.B * a.H, ns, a.Sq, a.Sk, a.nseg,
+              a.out_dtype == FP32 ? "fp32" : (a.out_dtype == BF16 ? "bf16" : "fp16"));
+  }
   if (!QB && !sparse && a.bias && a.bias_sq != 0) {
     // materialised [B|1,H|1,Q,K] bias or keep mask
     if (a.causal) {
@@ -1019,6 +1029,7 @@ hipError_t launch_qk_dump_d(const AttnArgs& a, hipStream_t s) {
   const int qtiles = (a.Sq + 127) / 128;
   const int total = qtiles * a.B * a.H;
   if (total == 0) return hipSuccess;
+  debug_log("attn_fwd_kernel<D=%d, score dump> grid %d x 256 Sq %d Sk %d", D, total, a.Sq, a.Sk);
   attn_fwd_kernel<D, BF16, 4, false, false, false, true><<<total, 256, 0, s>>>(a, qtiles, total);
   return hipGetLastError();
 }

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n)
 hipError_t launch_zero_words(void* p, int64_t words, hipStream_t s) {
   if (words <= 0) return hipSuccess;
   const int64_t blocks = (words + 255) / 256;
+  debug_log("zero_words_kernel grid %lld x 256 (words %lld)", (long long)(blocks < 4096 ? blocks : 4096), (long long)words);
   zero_words_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>((uint32_t*)p, words);
   return hipGetLastError();
 }
@@ -86,6 +87,9 @@ hipError_t launch_blockmask_to_index(const uint8_t* mask, int64_t rows, int64_t 
                                      hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((rows + 3) / 4);
+  debug_log("%s grid %u x 256 (rows %lld, Tk %lld)",
+            Tk % 16 == 0 && (uintptr_t)mask % 16 == 0 ? "blockmask_to_index16_kernel" : "blockmask_to_index_kernel", grid,
+            (long long)rows, (long long)Tk);
   if (Tk % 16 == 0 && (uintptr_t)mask % 16 == 0)
     blockmask_to_index16_kernel<<<grid, 256, 0, s>>>(mask, rows, Tk, index, count);
   else

@@ -106,6 +106,8 @@ hipError_t launch_split_combine(const CombineArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (int)(a.D / 8);
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  debug_log("split_combine_kernel<D=%lld> grid %u x 256 (rows %lld, splits %d)", (long long)a.D, grid, (long long)rows,
+            a.nsplit);
   if (a.D == 128) split_combine_kernel<128><<<grid, 256, 0, s>>>(a);
   else split_combine_kernel<64><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
@@ -116,6 +118,7 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (int)(a.D / 8);
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  debug_log("lse_merge_kernel<D=%lld> grid %u x 256 (rows %lld)", (long long)a.D, grid, (long long)rows);
   if (a.D == 128) lse_merge_kernel<128><<<grid, 256, 0, s>>>(a);
   else lse_merge_kernel<64><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -9,35 +9,51 @@ namespace qfa {
 
 enum DType : int { BF16 = 1, FP16 = 2, FP32 = 3, BOOL = 4 };
 
-// K mean: partial sums per (bh, chunk) in double-double, then one finalize.
-constexpr int kMeanChunkRows = 256;
+// Quantize step: K mean, then int8 codes of every Q and K row.
+//  - The K mean is summed in double-double partials over at most
+//    kMeanMaxChunks row chunks per (b, K/V head), at most kMeanSlots partials
+//    in all (fewer chunks per head when B*Hkv is large); a second small
+//    launch combines each head's partials into the mean. (Combining them in
+//    the last block of each head instead needs a device-scope fence in every
+//    block, an L2-wide write-back and invalidate that serialise per XCD: it
+//    measured 8x slower than the whole partial pass.)
+//  - One launch then quantizes all K rows (centred) and all Q rows.
+constexpr int kMeanMaxChunks = 64;
+constexpr int64_t kMeanSlots = 4096;
+constexpr int64_t kMeanMinChunkRows = 256;
 
-struct MeanArgs {
+// chunks per (b, K/V head) of a call with BH = B*Hkv heads of Sk keys
+__host__ __device__ inline int kmean_chunks(int64_t BH, int64_t Sk) {
+  if (BH <= 0 || Sk <= 0) return 0;
+  int64_t p = (Sk + kMeanMinChunkRows - 1) / kMeanMinChunkRows;
+  if (p > kMeanMaxChunks) p = kMeanMaxChunks;
+  const int64_t cap = kMeanSlots / BH;
+  if (p > cap) p = cap;
+  return (int)(p < 1 ? 1 : p);
+}
+
+// workspace of a centring call: the partials [BH][chunks][D] (double2)
+__host__ __device__ inline int64_t quantize_workspace_size(int64_t BH, int64_t Sk, int64_t D) {
+  return BH > 0 && Sk > 0 ? BH * kmean_chunks(BH, Sk) * D * 16 : 0;
+}
+
+struct QuantArgs {
+  int dtype;                      // BF16 or FP16 (Q and K)
+  int64_t B, H, Hkv, Sq, Sk, D;
+  const void* q;
+  int64_t q_sb, q_sh, q_ss;
   const void* k;
-  int dtype;
-  int64_t B, H, S, D;
-  int64_t sb, sh, ss;
-  const int32_t* vbs;   // nullable
-  double2* partial;     // [B*H, nchunks, D] (hi, lo)
-  float* mean;          // [B*H, D]
-  int nchunks;
+  int64_t k_sb, k_sh, k_ss;
+  const int32_t* vbs;             // nullable: per-tile valid counts (Sq == Sk)
+  int8_t* q8;                     // [B*H*Sq, D]
+  float* qs;                      // [B*H*Sq]
+  float* qmu;                     // nullable [B*H*Sq] (centring only)
+  int8_t* k8;                     // [B*Hkv*Sk, D]
+  float* ks;                      // [B*Hkv*Sk]
+  float* kmean;                   // nullable [B*Hkv, D]: centre K
+  void* workspace;                // quantize_workspace_size bytes (centring with Sk > 0)
 };
-hipError_t launch_kmean(const MeanArgs& a, hipStream_t s);
-
-struct QuantRowsArgs {
-  const void* x;
-  int dtype;
-  int64_t B, H, S, D;
-  int64_t sb, sh, ss;
-  const float* mean;    // nullable: centre rows by mean[b, h / (H / mean_heads), :]
-  const float* qmu_mean;// nullable: compute qmu = x . qmu_mean[b, h / (H / mean_heads), :] into qmu
-  int64_t mean_heads;   // heads of mean / qmu_mean (K's heads; divides H)
-  const int32_t* vbs;   // nullable
-  int8_t* codes;        // [B*H*S, D]
-  float* scale;         // [B*H*S]
-  float* qmu;           // nullable [B*H*S]
-};
-hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 
 // Clears `words` 32-bit words with a fill kernel (never a memset node, so a
 // captured graph replays it faithfully).
@@ -115,6 +131,12 @@ struct CombineArgs {
   void* o; int o_dtype; int64_t o_sb, o_sh, o_ss; float* l;   // l nullable
 };
 hipError_t launch_split_combine(const CombineArgs& a, hipStream_t s);
+
+// Launch log: with the environment variable QFA_DEBUG set to a nonzero
+// value, every launch prints one line to stderr naming the kernel instance,
+// its grid and its arguments' shape. Checked once per process.
+bool debug_enabled();
+void debug_log(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
 // ---- device helpers ----------------------------------------------------------
 

@@ -7,8 +7,16 @@
 // issue #3 (symmetric [-127,127] codes, absmax and quantize loops over the
 // same (row, channel) decomposition).
 //
-// Both kernels are HBM-bound streaming passes: 16-byte loads, one row of D
-// channels spread over D/8 lanes, the row absmax reduced across those lanes.
+// Three launches, the two big ones HBM-bound streaming passes with 16-byte
+// loads and one row of D channels spread over D/8 lanes:
+//   kmean_partial_kernel   exact column sums of K over at most 64 row chunks
+//                          per (b, K/V head)
+//   kmean_finalize_kernel  each head's chunk sums combined (exactly, so in any
+//                          order) into the mean: a few KB per head
+//   quantize_kernel        every K row (centred), then every Q row (and q.mu):
+//                          one grid. K rows run in reverse order of the mean
+//                          pass, so the rows that pass read last, still held
+//                          in the 256 MB MALL, are read again first.
 #include "qfa_internal.h"
 
 #include <float.h>
@@ -27,7 +35,8 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
 // multiple of the smallest input ulp with a modest magnitude, so hi + lo holds
 // the exact sum whenever the data's bit span stays below ~100 bits (always for
 // fp16; bf16 data within a 2^+-40 magnitude band). Hence the result does not
-// depend on the reduction order.
+// depend on the reduction order. A NaN or +-inf input makes lo (and so the
+// mean) NaN.
 struct DD {
   double hi, lo;
   __device__ __forceinline__ void add(double x) {
@@ -48,24 +57,24 @@ __device__ __forceinline__ bool is_pad(const int32_t* vbs, int64_t j) {
   return vbs != nullptr && (int32_t)(j & 63) >= vbs[j >> 6];
 }
 
-// Partial column sums of K over one chunk of kMeanChunkRows rows of one (b,h).
-// 1-D grid over (b,h) x chunks; block: 256 threads = D/8 channel groups x
-// (2048/D) row slots, each slot loading 4 rows at a time (16 bytes each).
+// K mean, first pass. 1-D grid over (b, K/V head) x chunks of chunk_rows
+// rows; block: 256 threads = D/8 channel groups x (2048/D) row slots, each
+// slot loading 4 rows at a time. The block's exact column sums go to its
+// partial slot.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void kmean_partial_kernel(MeanArgs a) {
+__global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nchunks, int64_t chunk_rows) {
   constexpr int G = D / 8;          // lanes per row
   constexpr int RP = 256 / G;       // row slots per block
   constexpr int U = 4;              // rows per slot in flight
   __shared__ double2 red[RP][D];
 
-  const int bid = blockIdx.x;
-  const int chunk = bid % a.nchunks;
-  const int64_t bh = bid / a.nchunks;
-  const int64_t b = bh / a.H, h = bh % a.H;
+  const int chunk = (int)(blockIdx.x % nchunks);
+  const int64_t bh = blockIdx.x / nchunks;
+  const int64_t b = bh / a.Hkv, h = bh % a.Hkv;
   const int cg = threadIdx.x % G, rs = threadIdx.x / G;
-  const int64_t r0 = (int64_t)chunk * kMeanChunkRows;
-  const int64_t r1 = min(r0 + kMeanChunkRows, a.S);
-  const uint16_t* base = (const uint16_t*)a.k + b * a.sb + h * a.sh + cg * 8;
+  const int64_t r0 = chunk * chunk_rows;
+  const int64_t r1 = min(r0 + chunk_rows, a.Sk);
+  const uint16_t* base = (const uint16_t*)a.k + b * a.k_sb + h * a.k_sh + cg * 8;
 
   DD acc[8];
 #pragma unroll
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(MeanArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t jj = j + u * RP;
       const bool live = jj < r1 && !is_pad(a.vbs, jj);
-      w[u] = live ? *(const uint4*)(base + jj * a.ss) : make_uint4(0u, 0u, 0u, 0u);
+      w[u] = live ? *(const uint4*)(base + jj * a.k_ss) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -92,29 +101,30 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(MeanArgs a) {
   for (int c = threadIdx.x; c < D; c += 256) {
     DD s{0.0, 0.0};
     for (int r = 0; r < RP; ++r) s.add(DD{red[r][c].x, red[r][c].y});
-    a.partial[(bh * a.nchunks + chunk) * D + c] = make_double2(s.hi, s.lo);
+    ((double2*)a.workspace)[(bh * nchunks + chunk) * D + c] = make_double2(s.hi, s.lo);
   }
 }
 
-// mean[bh, c] = fp32( fp64(hi + lo) / n ) over the chunk partials. 1-D grid
-// over (b,h) x 32-channel groups; block: 32 channels x 8 slices of chunks,
-// the slices' exact partial sums combined in LDS.
-__global__ __launch_bounds__(256) void kmean_finalize_kernel(MeanArgs a) {
+// K mean, second pass: mean[bh, c] = fp32( fp64(exact sum) / n ), n = Sk or
+// max(1, sum(vbs)). 1-D grid over (b, K/V head) x 32-channel groups; block:
+// 32 channels x 8 slices of the head's chunks, combined in LDS.
+__global__ __launch_bounds__(256) void kmean_finalize_kernel(QuantArgs a, int nchunks) {
   __shared__ long long nsum[256];
   __shared__ double2 red[8][32];
   const int groups = (int)(a.D / 32);
   const int64_t bh = blockIdx.x / groups;
   const int c = (blockIdx.x % groups) * 32 + (int)threadIdx.x % 32;
   const int slice = threadIdx.x / 32;
+  const double2* partial = (const double2*)a.workspace;
   long long n = 0;
   if (a.vbs) {
-    const int64_t T = (a.S + 63) / 64;
+    const int64_t T = (a.Sk + 63) / 64;
     for (int64_t t = threadIdx.x; t < T; t += 256) n += a.vbs[t];
   }
   nsum[threadIdx.x] = n;
   DD s{0.0, 0.0};
-  for (int k = slice; k < a.nchunks; k += 8) {
-    const double2 p = a.partial[(bh * a.nchunks + k) * a.D + c];
+  for (int k = slice; k < nchunks; k += 8) {
+    const double2 p = partial[(bh * nchunks + k) * a.D + c];
     s.add(DD{p.x, p.y});
   }
   red[slice][threadIdx.x % 32] = make_double2(s.hi, s.lo);
@@ -126,79 +136,109 @@ __global__ __launch_bounds__(256) void kmean_finalize_kernel(MeanArgs a) {
   if (slice == 0) {
     DD t{0.0, 0.0};
     for (int k = 0; k < 8; ++k) t.add(DD{red[k][threadIdx.x].x, red[k][threadIdx.x].y});
-    long long cnt = a.vbs ? nsum[0] : a.S;
+    long long cnt = a.vbs ? nsum[0] : a.Sk;
     if (cnt < 1) cnt = 1;
     const double total = t.hi + t.lo;  // the exact sum rounded once to fp64
-    a.mean[bh * a.D + c] = (float)(total / (double)cnt);
+    a.kmean[bh * a.D + c] = (float)(total / (double)cnt);
   }
 }
 
-// One row of D channels per D/8 lanes; each lane owns 8 consecutive channels.
-// 1-D grid over (b,h) x row blocks of RPB*U rows; each lane loads its chunk of
-// U rows first, then quantizes them one by one.
+// Every K row, then every Q row. One row of D channels per D/8 lanes, each
+// lane owning 8 consecutive channels; a block covers RPB*U rows of one head,
+// each lane loading its U rows first and then quantizing them one by one.
+// Per row x (K rows centred first, x - mu in one fp32 subtraction):
+//   a = max |x|; a < 127*FLT_MIN -> codes 0, scale 0;
+//   else scale = a/127, inv = 127/a (both correctly rounded),
+//        code = clamp(rint(x*inv), -127, 127);
+//   a NaN or +-inf in the row -> codes 0, scale NaN (and q.mu NaN).
+// Q rows with centring also give qmu = sum_c x_c * mu_c (fp32).
 template <int DT, int D>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a, int rblocks) {
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a, int64_t k_blocks, int k_rblocks, int q_rblocks) {
   constexpr int G = D / 8;
   constexpr int RPB = 256 / G;
   constexpr int U = 4;
   const int cg = threadIdx.x % G;
-  const int64_t bh = blockIdx.x / rblocks;
-  const int64_t j0 = (int64_t)(blockIdx.x % rblocks) * (RPB * U) + threadIdx.x / G;
-  const int64_t b = bh / a.H, h = bh % a.H;
-  // the mean row of this row's K/V head (grouped-query: runs of H / mean_heads heads share one)
-  const int64_t mrow = b * a.mean_heads + (int)h / (int)(a.H / a.mean_heads);
-  const uint16_t* src = (const uint16_t*)a.x + b * a.sb + h * a.sh + cg * 8;
+  // block-uniform choice of the operand
+  const bool is_k = (int64_t)blockIdx.x < k_blocks;
+  const int64_t idx = is_k ? k_blocks - 1 - (int64_t)blockIdx.x : (int64_t)blockIdx.x - k_blocks;
+  const int rblocks = is_k ? k_rblocks : q_rblocks;
+  const int64_t bh = idx / rblocks;
+  const int64_t heads = is_k ? a.Hkv : a.H;
+  const int64_t S = is_k ? a.Sk : a.Sq;
+  const int64_t ss = is_k ? a.k_ss : a.q_ss;
+  const int64_t b = bh / heads, h = bh % heads;
+  // the K/V head of this row (grouped-query: runs of H / Hkv query heads share one)
+  const int64_t mrow = b * a.Hkv + (is_k ? h : h / (a.H / a.Hkv));
+  const float* mean = is_k ? a.kmean : nullptr;               // centre K rows
+  const float* qmu_mean = is_k ? nullptr : a.kmean;           // q.mu of Q rows
+  float* qmu_out = is_k || !a.kmean ? nullptr : a.qmu;
+  int8_t* codes = is_k ? a.k8 : a.q8;
+  float* scales = is_k ? a.ks : a.qs;
+  const uint16_t* src = (const uint16_t*)(is_k ? a.k : a.q) + b * (is_k ? a.k_sb : a.q_sb) +
+                        h * (is_k ? a.k_sh : a.q_sh) + cg * 8;
+  const int64_t j0 = (int64_t)(idx % rblocks) * (RPB * U) + threadIdx.x / G;
 
   uint4 w[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t j = j0 + u * RPB;
-    const bool live = j < a.S && !is_pad(a.vbs, j);
-    w[u] = live ? *(const uint4*)(src + j * a.ss) : make_uint4(0u, 0u, 0u, 0u);
+    const bool live = j < S && !is_pad(a.vbs, j);
+    w[u] = live ? *(const uint4*)(src + j * ss) : make_uint4(0u, 0u, 0u, 0u);
   }
   float qm[8], mm[8];
-  if (a.qmu_mean) {
-    const float4 m0 = *(const float4*)(a.qmu_mean + mrow * D + cg * 8);
-    const float4 m1 = *(const float4*)(a.qmu_mean + mrow * D + cg * 8 + 4);
+  if (qmu_mean) {
+    const float4 m0 = *(const float4*)(qmu_mean + mrow * D + cg * 8);
+    const float4 m1 = *(const float4*)(qmu_mean + mrow * D + cg * 8 + 4);
     qm[0] = m0.x; qm[1] = m0.y; qm[2] = m0.z; qm[3] = m0.w; qm[4] = m1.x; qm[5] = m1.y; qm[6] = m1.z; qm[7] = m1.w;
   }
-  if (a.mean) {
-    const float4 m0 = *(const float4*)(a.mean + mrow * D + cg * 8);
-    const float4 m1 = *(const float4*)(a.mean + mrow * D + cg * 8 + 4);
+  if (mean) {
+    const float4 m0 = *(const float4*)(mean + mrow * D + cg * 8);
+    const float4 m1 = *(const float4*)(mean + mrow * D + cg * 8 + 4);
     mm[0] = m0.x; mm[1] = m0.y; mm[2] = m0.z; mm[3] = m0.w; mm[4] = m1.x; mm[5] = m1.y; mm[6] = m1.z; mm[7] = m1.w;
   }
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t j = j0 + u * RPB;
-    if (j >= a.S) break;   // uniform across the row's G lanes (G divides 64)
-    const int64_t r = bh * a.S + j;
+    if (j >= S) break;   // uniform across the row's G lanes (G divides 64)
+    const int64_t r = bh * S + j;
     const bool pad = is_pad(a.vbs, j);
     float x[8];
     unpack8<DT>(w[u], x);   // zeros for a pad row
 
     float qmu = 0.0f;
-    if (a.qmu_mean) {
+    if (qmu_mean) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) qmu += x[i] * qm[i];
     }
-    if (a.mean) {
+    if (mean) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = __fsub_rn(x[i], mm[i]);  // one fp32 subtraction
     }
 
     float amax = 0.0f;
+    bool finite = true;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(x[i]));
+      finite = finite && fabsf(x[i]) <= FLT_MAX;   // false for NaN and +-inf
+    }
 #pragma unroll
     for (int off = G / 2; off > 0; off >>= 1) {
       amax = fmaxf(amax, __shfl_xor(amax, off, G));
-      if (a.qmu) qmu += __shfl_xor(qmu, off, G);
+      if (qmu_out) qmu += __shfl_xor(qmu, off, G);
     }
+    // a row with a non-finite element (on any of its G lanes, which are
+    // consecutive lanes of the wave) gets codes 0, scale NaN and a NaN
+    // centring term; the rows of lanes that left the loop are absent from
+    // the ballot and do not matter here
+    const uint64_t bad_lanes = __ballot(!finite);
+    const int row_lane0 = (int)(threadIdx.x % 64) & ~(G - 1);
+    const bool bad_row = ((bad_lanes >> row_lane0) & ((1ull << G) - 1ull)) != 0ull;   // G <= 16
 
     uint32_t lo = 0, hi = 0;
-    float scale = 0.0f;
-    if (!pad && amax >= 127.0f * FLT_MIN) {
+    float scale = bad_row ? __builtin_nanf("") : 0.0f;
+    if (!pad && !bad_row && amax >= 127.0f * FLT_MIN) {
       scale = amax / 127.0f;                  // correctly rounded fp32 division
       const float inv = 127.0f / amax;
 #pragma unroll
@@ -210,45 +250,54 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a, int
         else hi |= code << (8 * (i - 4));
       }
     }
-    *(uint2*)(a.codes + r * D + cg * 8) = make_uint2(lo, hi);
+    *(uint2*)(codes + r * D + cg * 8) = make_uint2(lo, hi);
     if (cg == 0) {
-      a.scale[r] = scale;
-      if (a.qmu) a.qmu[r] = pad ? 0.0f : qmu;
+      scales[r] = scale;
+      if (qmu_out) qmu_out[r] = pad ? 0.0f : (bad_row ? __builtin_nanf("") : qmu);
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_kmean(const MeanArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.nchunks * a.B * a.H);
-  if (grid == 0) return hipSuccess;   // no (b,h) pair or no rows: nothing to average
-  if (a.D == 128) {
-    if (a.dtype == BF16) kmean_partial_kernel<BF16, 128><<<grid, 256, 0, s>>>(a);
-    else kmean_partial_kernel<FP16, 128><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (a.dtype == BF16) kmean_partial_kernel<BF16, 64><<<grid, 256, 0, s>>>(a);
-    else kmean_partial_kernel<FP16, 64><<<grid, 256, 0, s>>>(a);
+template <int DT, int D>
+hipError_t launch_dt_d(const QuantArgs& a, hipStream_t s) {
+  const char* dn = DT == BF16 ? "bf16" : "fp16";
+  const int64_t BHk = a.B * a.Hkv;
+  if (a.kmean && a.Sk > 0 && BHk > 0) {
+    const int nchunks = kmean_chunks(BHk, a.Sk);
+    const int64_t chunk_rows = (a.Sk + nchunks - 1) / nchunks;
+    const unsigned grid = (unsigned)(BHk * nchunks);
+    debug_log("kmean_partial_kernel<%s, D=%d> grid %u x 256 (B*Hkv %lld, %d chunks of %lld rows); "
+              "kmean_finalize_kernel grid %lld x 256", dn, D, grid, (long long)BHk, nchunks, (long long)chunk_rows,
+              (long long)(BHk * (D / 32)));
+    kmean_partial_kernel<DT, D><<<grid, 256, 0, s>>>(a, nchunks, chunk_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kmean_finalize_kernel<<<(unsigned)(BHk * (D / 32)), 256, 0, s>>>(a, nchunks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (a.kmean && BHk > 0) {
+    // no keys: the mean of nothing is 0 (the count is clamped to 1)
+    const hipError_t e = launch_zero_words(a.kmean, BHk * D, s);
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  kmean_finalize_kernel<<<(unsigned)(a.B * a.H * (a.D / 32)), 256, 0, s>>>(a);
+  constexpr int rpb = 4 * (256 / (D / 8));   // rows per block: 4 per row slot
+  const int k_rblocks = (int)((a.Sk + rpb - 1) / rpb);
+  const int q_rblocks = (int)((a.Sq + rpb - 1) / rpb);
+  const int64_t k_blocks = BHk * k_rblocks;
+  const int64_t grid = k_blocks + a.B * a.H * q_rblocks;
+  if (grid == 0) return hipSuccess;
+  debug_log("quantize_kernel<%s, D=%d> grid %lld x 256 (K rows %lld in %lld blocks, centred %d; Q rows %lld, qmu %d)",
+            dn, D, (long long)grid, (long long)(BHk * a.Sk), (long long)k_blocks, a.kmean != nullptr,
+            (long long)(a.B * a.H * a.Sq), a.kmean != nullptr && a.qmu != nullptr);
+  quantize_kernel<DT, D><<<(unsigned)grid, 256, 0, s>>>(a, k_blocks, k_rblocks, q_rblocks);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s) {
-  const int rpb = 4 * (256 / (int)(a.D / 8));   // rows per block: 4 per row slot
-  const int rblocks = (int)((a.S + rpb - 1) / rpb);
-  const unsigned grid = (unsigned)(rblocks * a.B * a.H);
-  if (grid == 0) return hipSuccess;
-  if (a.D == 128) {
-    if (a.dtype == BF16) quantize_rows_kernel<BF16, 128><<<grid, 256, 0, s>>>(a, rblocks);
-    else quantize_rows_kernel<FP16, 128><<<grid, 256, 0, s>>>(a, rblocks);
-  } else {
-    if (a.dtype == BF16) quantize_rows_kernel<BF16, 64><<<grid, 256, 0, s>>>(a, rblocks);
-    else quantize_rows_kernel<FP16, 64><<<grid, 256, 0, s>>>(a, rblocks);
-  }
-  return hipGetLastError();
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  if (a.D == 128) return a.dtype == BF16 ? launch_dt_d<BF16, 128>(a, s) : launch_dt_d<FP16, 128>(a, s);
+  return a.dtype == BF16 ? launch_dt_d<BF16, 64>(a, s) : launch_dt_d<FP16, 64>(a, s);
 }
 
 }  // namespace qfa

@@ -33,8 +33,14 @@ def test_exports_every_declared_symbol():
 
 
 def test_workspace_size():
+    """K-mean partials: up to 64 chunks of at least 256 rows per (b, K/V head), at most 4096 in all,
+    16 bytes per channel."""
     n = qfa.quantize_workspace_bytes(1, 56, 33600, 128)
-    assert n == 56 * ((33600 + 255) // 256) * 128 * 16
+    assert n == 56 * 64 * 128 * 16                    # 132 chunks of 256 rows capped at 64
+    assert qfa.quantize_workspace_bytes(1, 20, 9216, 64) == 20 * 36 * 64 * 16
+    assert qfa.quantize_workspace_bytes(8, 128, 4096, 128) == 1024 * 4 * 128 * 16   # 4096 slots in all
+    assert qfa.quantize_workspace_bytes(1, 5000, 300, 64) == 5000 * 64 * 16          # one chunk each
+    assert qfa.quantize_workspace_bytes(1, 3, 100, 64) == 3 * 64 * 16
     assert qfa.quantize_workspace_bytes(1, 1, 0, 64) == 0
 
 
@@ -69,7 +75,8 @@ def _attn(**kw):
              bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None, causal=0,
              out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
     a.update(kw)
-    return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a.get("Hkv", a["H"]), a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"], a["vdt"], *a["v_s"],
+    return _lib.lib().qfa_attn_fwd(a["B"], a["H"], a.get("Hkv", a["H"]), a["Sq"], a["Sk"], a["D"], *a["qk"],
+                                   a.get("centered", 1), a["v"], a["vdt"], *a["v_s"],
                                    ctypes.c_float(a["scale"]), a["bias"], a["bdt"], *a["b_s"], a.get("bsq", 0), a["index"],
                                    a["count"], a["vbs"], a["vsc"], a["nseg"], a["seg"], a["causal"], a["out"], a["odt"],
                                    *a["o_s"], a["lse"], None)
@@ -80,7 +87,8 @@ def _attn_split(ns, ws=FAKE, wsb=1 << 30, **kw):
              bias=None, bdt=3, b_s=(0, 0), index=None, count=None, vbs=None, vsc=None, nseg=0, seg=None, causal=0,
              out=FAKE, odt=1, o_s=(32768, 16384, 128), lse=None)
     a.update(kw)
-    return _lib.lib().qfa_attn_fwd_splitk(a["B"], a["H"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"], a["v"],
+    return _lib.lib().qfa_attn_fwd_splitk(a["B"], a["H"], a["H"], a["Sq"], a["Sk"], a["D"], *a["qk"],
+                                          a.get("centered", 1), a["v"],
                                           a["vdt"], *a["v_s"], ctypes.c_float(a["scale"]), a["bias"], a["bdt"],
                                           *a["b_s"], 0, a["index"], a["count"], a["vbs"], a["vsc"], a["nseg"],
                                           a["seg"], a["causal"], a["out"], a["odt"], *a["o_s"], a["lse"], ns, ws,
@@ -168,6 +176,24 @@ def test_attn_rejects_bad_arguments():
     for hkv in (0, 3, 4, -1):
         assert _attn(Hkv=hkv) == _lib.QFA_ERR_INVALID_ARG
     assert b"K/V heads" in _lib.lib().qfa_last_error()
+
+
+def test_attn_centring_term_guard():
+    """On codes of centred K the LSE needs the centring term sm_scale * q.mu: a call asking for the LSE
+    without qmu is refused before any launch, and so is a qmu passed for uncentred codes."""
+    L = _lib.lib()
+    no_qmu = [FAKE, FAKE, None, FAKE, FAKE]
+    assert _attn(qk=no_qmu, lse=FAKE) == _lib.QFA_ERR_INVALID_ARG
+    assert b"centring term" in L.qfa_last_error()
+    assert _attn_split(2, qk=no_qmu, lse=FAKE) == _lib.QFA_ERR_INVALID_ARG
+    assert _attn(qk=[FAKE] * 5, centered=0) == _lib.QFA_ERR_INVALID_ARG
+    assert b"not centred" in L.qfa_last_error()
+    # without the LSE, or on uncentred codes, qmu is not needed: these fail only on a later check
+    # (a zero softmax scale), which shows they passed the guard
+    assert _attn(qk=no_qmu, scale=0.0) == _lib.QFA_ERR_INVALID_ARG
+    assert b"sm_scale" in L.qfa_last_error()
+    assert _attn(qk=no_qmu, centered=0, lse=FAKE, scale=0.0) == _lib.QFA_ERR_INVALID_ARG
+    assert b"sm_scale" in L.qfa_last_error()
 
 
 def test_merge_rejects_bad_arguments():

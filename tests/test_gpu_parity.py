@@ -1,17 +1,23 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
 Quantized codes, scales, K mean, tile-index lists: bit-exact. Attention
-output: max-abs <= 2e-2 and mean-abs <= 2e-3 (fp32); LSE <= 1e-3 absolute.
-Sizes span several 128-query and 64-key tiles plus ragged tails; the
-full-size workloads are checked on sampled rows the oracle computes one by one.
+output: every call runs with an fp32 output, checked at max-abs <= 2e-2 and
+mean-abs <= 2e-3, and with V's 16-bit type, which must equal the fp32 output
+rounded to nearest even bit for bit; LSE <= 1e-3 absolute. Sizes span several
+128-query and 64-key tiles plus ragged tails; the dense 4k and d64 workloads
+are compared on every row, the banded and block-sparse ones on rows of every
+head and every 128-row query block.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import DEV, O_MAX_ABS, as_bshd, check_lse, check_o, down, sample_rows, up
+from tests.gpu_util import (DEV, O_MAX_ABS, as_bshd, block_rows, both_outputs, check_lse, check_o, check_rne, down,
+                            sample_rows, up)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,18 +150,22 @@ def test_quantize_full_size(name):
 
 # --------------------------------------------------------------- attention --
 
-def _attn_case(w, q, k, v, *, bias=None, segments=None, vsc=None, out_dtype=None, bshd=False, rows=None):
+def _attn_case(w, q, k, v, *, bias=None, segments=None, vsc=None, bshd=False, rows=None):
+    """One call with an fp32 output and one with V's type (checked against each other by RNE);
+    returns the fp32 output and LSE with the oracle's."""
     ref = oracle.quantize_qk(q, k)
     g = gpu_quant(q, k)
     tv = up(v)
     if bshd:
         tv = as_bshd(tv)
-    out = None
-    if bshd:
-        B, H, Sq, D = q.shape
-        out = torch.empty((B, Sq, H, D), dtype=out_dtype or tv.dtype, device=DEV).transpose(1, 2)
-    o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=None if bias is None else up(bias), segments=segments,
-                        v_scale=None if vsc is None else up(vsc), out=out, out_dtype=out_dtype, return_lse=True)
+    B, H, Sq, D = q.shape
+
+    def call(dt):
+        out = torch.empty((B, Sq, H, D), dtype=dt, device=DEV).transpose(1, 2) if bshd else None
+        return qfa.attn_fwd(g, tv, w.sm_scale, bias=None if bias is None else up(bias), segments=segments,
+                            v_scale=None if vsc is None else up(vsc), out=out, out_dtype=dt, return_lse=True)
+
+    o, l = both_outputs(call, tv.dtype)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, segments=segments, v_scale=vsc, rows=rows)
     return o, l, o_ref, l_ref
 
@@ -168,7 +178,7 @@ ATTN_CASES = {
     "band_bias_bf16": dict(w="band", H=2, Sq=256, Sk=2100, bias="bf16"),
     "band_bias_fp16": dict(w="band", H=1, Sq=130, Sk=700, bias="fp16"),
     "band_segments": dict(w="band", H=2, Sq=200, Sk=2100, bias="fp32", segments=[(3, 600), (700, 1), (1500, 599)]),
-    "vscale_fp32_out": dict(w="sparse", H=2, Sq=192, Sk=192, vscale=True, out_dtype=torch.float32),
+    "vscale": dict(w="sparse", H=2, Sq=192, Sk=192, vscale=True),
     "bshd_views": dict(w="tiny", bshd=True, bias="fp32"),
 }
 
@@ -180,7 +190,6 @@ def test_attn_parity(case):
     bias_dt = c.pop("bias", None)
     segments = c.pop("segments", None)
     vscale = c.pop("vscale", False)
-    out_dtype = c.pop("out_dtype", None)
     bshd = c.pop("bshd", False)
     q, k, v = W.make_qkv(w, **c)
     Sk = k.shape[2]
@@ -192,10 +201,7 @@ def test_attn_parity(case):
         else:
             bias = W.bias_tensor(b64, bias_dt)
     vsc = W.v_scale(w, H=q.shape[1]) if vscale else None
-    o, l, o_ref, l_ref = _attn_case(w, q, k, v, bias=bias, segments=segments, vsc=vsc, out_dtype=out_dtype,
-                                    bshd=bshd)
-    if out_dtype is not None:
-        assert o.dtype == out_dtype
+    o, l, o_ref, l_ref = _attn_case(w, q, k, v, bias=bias, segments=segments, vsc=vsc, bshd=bshd)
     check_o(o, o_ref, what=case)
     check_lse(l, l_ref, what=case)
 
@@ -267,8 +273,9 @@ def test_keep_mask():
         keep4 = keep.reshape(1, 1, 1, Sk)
         add = np.where(keep4, 0.0, -np.inf).astype(np.float32)
         o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=add, segments=seg)
-        o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=torch.from_numpy(keep4).to(tv.device), segments=seg,
-                            return_lse=True)
+        tb = torch.from_numpy(keep4).to(tv.device)
+        o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, segments=seg, out_dtype=dt,
+                                                    return_lse=True), tv.dtype, what)
         check_o(o, o_ref, what=what)
         check_lse(l, l_ref, what=what)
 
@@ -306,7 +313,9 @@ def test_causal_parity(case, lse):
         bias_ref = np.where(keep, 0.0, -np.inf).astype(np.float32)
         bias_gpu = torch.from_numpy(keep).to(DEV)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias_ref, causal=True)
-    res = qfa.attn_fwd(g, up(v), w.sm_scale, bias=bias_gpu, causal=True, return_lse=lse)
+    tv = up(v)
+    res = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=bias_gpu, causal=True, out_dtype=dt,
+                                               return_lse=lse), tv.dtype, case)
     o = res[0] if lse else res
     check_o(o, o_ref, what=f"causal {case}")
     if lse:
@@ -316,15 +325,18 @@ def test_causal_parity(case, lse):
 
 
 def test_causal_full_size_sampled():
-    """B1 H16 S4096 D128 causal: sampled rows plus the rows around block and tile edges."""
+    """B1 H16 S4096 D128 causal: two rows of every 128-row block of every head, plus the rows around
+    block and tile edges."""
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w)
     ref = oracle.quantize_qk(q, k)
     g = gpu_quant(q, k)
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=24)
+    rows = block_rows(w.B, w.H, w.Sq, per_block=2, seed=3)
     edges = np.array([0, 1, 63, 64, 127, 128, 129, 2047, 2048, 4031, 4032, 4095])
     rows = np.unique(np.r_[rows, edges, 5 * w.Sq + edges])
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, causal=True, return_lse=True)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, causal=True, out_dtype=dt, return_lse=True),
+                        tv.dtype, "causal full")
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows, causal=True)
     check_o(o, o_ref, rows, "causal full")
     check_lse(l, l_ref, rows, "causal full")
@@ -356,10 +368,11 @@ def test_gqa_parity(case):
     causal = opt.get("causal", False)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, v_scale=vsc, causal=causal)
     kw = dict(bias=None if bias is None else up(bias), v_scale=None if vsc is None else up(vsc), causal=causal)
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, **kw)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True, out_dtype=dt, **kw), tv.dtype, case)
     check_o(o, o_ref, what=case)
     check_lse(l, l_ref, what=case)
-    o2 = qfa.attn_fwd(g, up(v), w.sm_scale, **kw)
+    o2 = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt, **kw), tv.dtype, case)
     check_o(o2, o_ref, what=case + " no LSE")
 
 
@@ -376,14 +389,17 @@ def test_gqa_sparse():
 
 
 def test_gqa_full_size_sampled():
-    """B2 S2048 H16 Hkv2 D128 causal (the grouped-query shape of the FlyDSL table), sampled rows."""
+    """B2 S2048 H16 Hkv2 D128 causal (the grouped-query shape of the FlyDSL table): a row of every
+    128-row block of every (b, h)."""
     w = W.WORKLOADS["gqa"]
     q, k, v = W.make_qkv(w)
     ref = oracle.quantize_qk(q, k)
     g = gpu_quant(q, k)
     assert_quant_equal(g, ref)
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=16, heads=[0, 7, 8, 15])
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, causal=True, return_lse=True)
+    rows = block_rows(w.B, w.H, w.Sq, per_block=1, seed=4)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, causal=True, out_dtype=dt, return_lse=True),
+                        tv.dtype, "gqa full")
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows, causal=True)
     check_o(o, o_ref, rows, "gqa full")
     check_lse(l, l_ref, rows, "gqa full")
@@ -424,24 +440,24 @@ def test_split_k_parity(case):
         bias_gpu = torch.from_numpy(keep).to(DEV)
     vsc = W.v_scale(w, H=Hkv) if opt.get("vscale") else None
     seg, causal = opt.get("segments"), opt.get("causal", False)
-    out_dtype = torch.float32 if opt.get("fp32out") else None
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias_ref, v_scale=vsc, segments=seg, causal=causal)
-    kw = dict(bias=bias_gpu, v_scale=None if vsc is None else up(vsc), segments=seg, causal=causal,
-              out_dtype=out_dtype)
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, splits=ns, **kw)
+    kw = dict(bias=bias_gpu, v_scale=None if vsc is None else up(vsc), segments=seg, causal=causal)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True, splits=ns, out_dtype=dt, **kw),
+                        tv.dtype, case)
     check_o(o, o_ref, what=case)
     check_lse(l, l_ref, what=case)
-    o2 = qfa.attn_fwd(g, up(v), w.sm_scale, splits=ns, **kw)
+    o2 = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, splits=ns, out_dtype=dt, **kw), tv.dtype, case)
     check_o(o2, o_ref, what=case + " no LSE")
-    o1, l1 = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True, **kw)
-    assert (o.float() - o1.float()).abs().max().item() <= 2e-2
+    o1, l1 = qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True, out_dtype=torch.float32, **kw)
+    assert (o - o1).abs().max().item() <= 2e-2
     fin = torch.isfinite(l1)
     assert torch.equal(fin, torch.isfinite(l)) and (l[fin] - l1[fin]).abs().max().item() <= 1e-3
 
 
 def test_split_k_band_shard_sampled():
     """The banded workload's per-GPU shard with 7 heads (B1 H7 Sq4096 Sk33600, 224 query
-    blocks for 256 CUs) with the library's own split count, on sampled rows."""
+    blocks for 256 CUs) with the library's own split count, on a row of every 128-row block."""
     w = W.WORKLOADS["band"]
     q, k, v = W.make_qkv(w, H=7)
     ref = oracle.quantize_qk(q, k)
@@ -449,9 +465,11 @@ def test_split_k_band_shard_sampled():
     ns = qfa.splits_auto(1, 7, w.Sq, w.Sk)
     assert ns > 1
     bias = W.bias_tensor(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]), "fp32")
-    rows = sample_rows(w.B, 7, w.Sq, per_head=24, heads=[0, 6])
+    rows = block_rows(w.B, 7, w.Sq, per_block=1, seed=6)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, bias=up(bias), return_lse=True, splits="auto")
+    tv, tb = up(v), up(bias)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, return_lse=True, splits="auto", out_dtype=dt),
+                        tv.dtype, "band shard")
     check_o(o, o_ref, rows, f"band shard, {ns} splits")
     check_lse(l, l_ref, rows, f"band shard, {ns} splits")
 
@@ -485,10 +503,12 @@ def test_unquant_parity(case):
         tq, tk, tv = as_bshd(tq), as_bshd(tk), as_bshd(tv)
     kw = dict(bias=None if bias is None else up(bias), v_scale=None if vsc is None else up(vsc), segments=seg,
               causal=causal, splits=opt.get("splits"))
-    o, l = qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, return_lse=True, **kw)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, return_lse=True, out_dtype=dt, **kw),
+                        tv.dtype, case)
     check_o(o, o_ref, what=case)
     check_lse(l, l_ref, what=case)
-    check_o(qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, **kw), o_ref, what=case + " no LSE")
+    o2 = both_outputs(lambda dt: qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, out_dtype=dt, **kw), tv.dtype, case)
+    check_o(o2, o_ref, what=case + " no LSE")
 
 
 def test_unquant_sparse():
@@ -503,7 +523,9 @@ def test_unquant_sparse():
         W.zero_pads(x, vbs)
     o_ref, l_ref = oracle.attn(None, v, w.sm_scale, q=W.to_f32(q), k=W.to_f32(k), mask=mask, vbs=vbs)
     idx, cnt = qfa.blockmask_to_index(up(mask))
-    o, l = qfa.attn_fwd_unquant(up(q), up(k), up(v), w.sm_scale, index=idx, count=cnt, vbs=up(vbs), return_lse=True)
+    tq, tk, tv, tvbs = up(q), up(k), up(v), up(vbs)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd_unquant(tq, tk, tv, w.sm_scale, index=idx, count=cnt, vbs=tvbs,
+                                                        out_dtype=dt, return_lse=True), tv.dtype, "unquant sparse")
     check_o(o, o_ref, what="unquant sparse")
     check_lse(l, l_ref, what="unquant sparse")
 
@@ -514,8 +536,9 @@ def test_unquant_error_below_int8_error():
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w, H=2, Sq=512, Sk=2048)
     exact, _ = oracle.attn(None, v, w.sm_scale, q=W.to_f32(q), k=W.to_f32(k))
-    o8 = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale).float().cpu().numpy().reshape(-1, 128)
-    ob = qfa.attn_fwd_unquant(up(q), up(k), up(v), w.sm_scale).float().cpu().numpy().reshape(-1, 128)
+    f32 = torch.float32
+    o8 = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, out_dtype=f32).cpu().numpy().reshape(-1, 128)
+    ob = qfa.attn_fwd_unquant(up(q), up(k), up(v), w.sm_scale, out_dtype=f32).cpu().numpy().reshape(-1, 128)
     e8, eb = np.abs(o8 - exact), np.abs(ob - exact)
     assert eb.mean() < e8.mean(), (eb.mean(), e8.mean())
     assert eb.max() <= O_MAX_ABS
@@ -571,7 +594,9 @@ def test_bias2d_parity(case):
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, causal=causal)
     g = gpu_quant(q, k)
     lse = opt.get("lse", True)
-    res = qfa.attn_fwd(g, up(v), w.sm_scale, bias=dev_b, causal=causal, splits=opt.get("splits"), return_lse=lse)
+    tv = up(v)
+    res = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=dev_b, causal=causal, splits=opt.get("splits"),
+                                               out_dtype=dt, return_lse=lse), tv.dtype, case)
     o = res[0] if lse else res
     check_o(o, o_ref, what=case)
     if lse:
@@ -610,21 +635,26 @@ def test_bias2d_row_tail(kind, Sk):
         dev_b = up(full)[..., :Sk]
     ref = oracle.quantize_qk(q, k)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b)
-    o, l = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, bias=dev_b, return_lse=True)
     what = f"{kind} Sk={Sk}"
+    g, tv = gpu_quant(q, k), up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=dev_b, out_dtype=dt, return_lse=True),
+                        tv.dtype, what)
     check_o(o, o_ref, what=what)
     check_lse(l, l_ref, what=what)
 
 
 def test_bias2d_full_size_sampled():
-    """B1 H16 S4096 D128 with a materialised bf16 [1,1,4096,4096] bias, sampled rows."""
+    """B1 H16 S4096 D128 with a materialised bf16 [1,1,4096,4096] bias: a row of every 128-row block of
+    every head."""
     w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w)
     ref_b, dev_b = _bias2d("bf16", 1, 1, w.Sq, w.Sk, seed=7)
     ref = oracle.quantize_qk(q, k)
     g = gpu_quant(q, k)
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=16)
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, bias=dev_b, return_lse=True)
+    rows = block_rows(w.B, w.H, w.Sq, per_block=1, seed=7)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=dev_b, out_dtype=dt, return_lse=True),
+                        tv.dtype, "bias2d full")
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, rows=rows)
     check_o(o, o_ref, rows, "bias2d full")
     check_lse(l, l_ref, rows, "bias2d full")
@@ -652,7 +682,7 @@ def test_split_merge_small():
     o_c, l_c = qfa.attn_fwd(g, tv, w.sm_scale, segments=[core], out_dtype=torch.float32, return_lse=True)
     o_s, l_s = qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, segments=[(0, skirt), (core[0] + core[1], skirt)],
                             out_dtype=torch.float32, return_lse=True)
-    o_m, l_m = qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
+    o_m, l_m = both_outputs(lambda dt: qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=dt), torch.bfloat16, "merge")
     check_o(o_m, o_ref, what="split+merge")
     check_lse(l_m, l_ref, what="split+merge")
     # the merge kernel itself against the oracle's merge of the same partials
@@ -718,7 +748,9 @@ def _sparse_case(T, H, mask, vbs, rows=None, Hkv=None):
     g = gpu_quant(q, k, vbs)
     assert_quant_equal(g, ref)
     idx, cnt = qfa.blockmask_to_index(up(mask))
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, index=idx, count=cnt, vbs=up(vbs), v_scale=up(vsc), return_lse=True)
+    tv, tvbs, tvsc = up(v), up(vbs), up(vsc)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, index=idx, count=cnt, vbs=tvbs, v_scale=tvsc,
+                                                out_dtype=dt, return_lse=True), tv.dtype, "sparse")
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, mask=mask, vbs=vbs, v_scale=vsc, rows=rows)
     return o, l, o_ref, l_ref
 
@@ -765,7 +797,8 @@ def test_sparse_band_structure():
 # --------------------------------------------------- full-size, sampled rows --
 
 def test_band_full_size_sampled():
-    """B1 H56 Sq4096 Sk33600 D128: unmasked, fp32 bias, bf16 bias and core+skirt split, as timed."""
+    """B1 H56 Sq4096 Sk33600 D128: unmasked, fp32 bias, bf16 bias and core+skirt split, as timed, on
+    two rows of every 128-row query block of every head."""
     w = W.WORKLOADS["band"]
     q, k, v = W.make_qkv(w)
     core, skirt = w.extras["core"], w.extras["skirt"]
@@ -774,50 +807,76 @@ def test_band_full_size_sampled():
     g = gpu_quant(q, k)
     assert_quant_equal(g, ref)
     tv = up(v)
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=24, heads=[0, 13, 55])
-    o, l = qfa.attn_fwd(g, tv, w.sm_scale, return_lse=True)
+    rows = block_rows(w.B, w.H, w.Sq, per_block=2, seed=5)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt, return_lse=True), tv.dtype,
+                        "unmasked")
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows)
     check_o(o, o_ref, rows, "unmasked")
     check_lse(l, l_ref, rows, "unmasked")
-    for dt in ("fp32", "bf16"):
-        bias = W.bias_tensor(b64, dt)
-        o, l = qfa.attn_fwd(g, tv, w.sm_scale, bias=up(bias), return_lse=True)
-        o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
-        check_o(o, o_ref, rows, f"bias {dt}")
-        check_lse(l, l_ref, rows, f"bias {dt}")
-    bias = W.bias_tensor(b64, "fp32")
-    tb = up(bias)
+    del o, l
+    refs = {}
+    for dt_b in ("fp32", "bf16"):
+        bias = W.bias_tensor(b64, dt_b)
+        tb = up(bias)
+        o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, out_dtype=dt, return_lse=True),
+                            tv.dtype, f"bias {dt_b}")
+        refs[dt_b] = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
+        check_o(o, refs[dt_b][0], rows, f"bias {dt_b}")
+        check_lse(l, refs[dt_b][1], rows, f"bias {dt_b}")
+        del o, l
+    # the split of the fp32-bias call: core unmasked + skirts with the bias, merged by LSE
+    o_ref, l_ref = refs["fp32"]
+    tb = up(W.bias_tensor(b64, "fp32"))
     o_c, l_c = qfa.attn_fwd(g, tv, w.sm_scale, segments=[core], out_dtype=torch.float32, return_lse=True)
     o_s, l_s = qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, segments=[(0, skirt), (core[0] + core[1], skirt)],
                             out_dtype=torch.float32, return_lse=True)
-    o_m, l_m = qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=torch.bfloat16)
-    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=bias, rows=rows)
+    o_m, l_m = both_outputs(lambda dt: qfa.lse_merge(o_c, l_c, o_s, l_s, out_dtype=dt), torch.bfloat16, "merge")
     check_o(o_m, o_ref, rows, "split+merge")
     check_lse(l_m, l_ref, rows, "split+merge")
 
 
-@pytest.mark.parametrize("name", ["dense4k", "d64"])
-def test_dense_full_size_sampled(name):
-    w = W.WORKLOADS[name]
+@pytest.mark.parametrize("lse", [False, True])
+def test_dense4k_full_size_every_row(lse):
+    """B1 H16 S4096 D128 bf16 with the per-channel K offset: every row of every head, LSE off and on
+    (different kernel instances)."""
+    w = W.WORKLOADS["dense4k"]
     q, k, v = W.make_qkv(w)
     ref = oracle.quantize_qk(q, k)
     g = gpu_quant(q, k)
     assert_quant_equal(g, ref)
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=32)
-    o, l = qfa.attn_fwd(g, up(v), w.sm_scale, return_lse=True)
-    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows)
-    check_o(o, o_ref, rows, name)
-    check_lse(l, l_ref, rows, name)
+    tv = up(v)
+    res = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt, return_lse=lse), tv.dtype, "dense4k")
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale)
+    check_o(res[0] if lse else res, o_ref, what="dense4k all rows")
+    if lse:
+        check_lse(res[1], l_ref, what="dense4k all rows")
+
+
+def test_d64_full_size_every_row():
+    """B2 H10 S9216 D64 fp16: every row of every (b, h), with the LSE."""
+    w = W.WORKLOADS["d64"]
+    q, k, v = W.make_qkv(w)
+    ref = oracle.quantize_qk(q, k)
+    g = gpu_quant(q, k)
+    assert_quant_equal(g, ref)
+    tv = up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt, return_lse=True), tv.dtype, "d64")
+    o_ref, l_ref = oracle.attn(ref, v, w.sm_scale)
+    check_o(o, o_ref, what="d64 all rows")
+    check_lse(l, l_ref, what="d64 all rows")
 
 
 def test_sparse_full_size_sampled():
-    """B1 H24 S131072 D128, prefix-8 + band-48 tile mask, vbs last tile 17, V scale."""
+    """B1 H24 S131072 D128, prefix-8 + band-48 tile mask, vbs last tile 17, V scale: a row of every
+    128-row block (a block-sparse block's pair of query tiles) of every head, and every row of the
+    ragged last tile of two heads, pad rows included."""
     w = W.WORKLOADS["sparse"]
     T = w.Sk // 64
     mask = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
     vbs = W.sparse_vbs(T, w.extras["last_valid"])
-    rows = sample_rows(w.B, w.H, w.Sq, per_head=24, heads=[0, 23])
-    rows = np.unique(np.r_[rows, w.Sq - 1 - np.arange(64)])  # the ragged last tile incl. pad rows
+    rows = block_rows(w.B, w.H, w.Sq, per_block=1, seed=8)
+    last = w.Sq - 1 - np.arange(64)
+    rows = np.unique(np.r_[rows, last, (w.H - 1) * w.Sq + last])
     o, l, o_ref, l_ref = _sparse_case(T, w.H, mask, vbs, rows=rows)
     check_o(o, o_ref, rows, "sparse full")
     check_lse(l, l_ref, rows, "sparse full")
@@ -975,17 +1034,20 @@ def test_offsets_past_2_31_elements():
     g = qfa.quantize_qk(q, k)
     sm = float(np.float32(D ** -0.5))
     seg = [(S - 1000, 1000)]
-    o, lse = qfa.attn_fwd(g, v, sm, segments=seg, return_lse=True)
+    o, lse = qfa.attn_fwd(g, v, sm, segments=seg, out_dtype=torch.float32, return_lse=True)
+    o16, lse16 = qfa.attn_fwd(g, v, sm, segments=seg, return_lse=True)   # the same instance, bf16 output
     torch.cuda.synchronize()
     rows = np.r_[0:32, S - 32:S]
+    assert torch.equal(lse, lse16)
     for h in (0, H - 1):
+        check_rne(o16[0, h], o[0, h], f"head {h}")
         qh, kh, vh = (down(t[:, h:h + 1]) for t in (q, k, v))
         ref = oracle.quantize_qk(qh, kh)
         assert_quant_equal({n: g[n][:, h:h + 1] for n in ("q8", "qs", "k8", "ks", "kmean", "qmu")}, ref)
         o_ref, l_ref = oracle.attn(ref, vh, sm, segments=seg, rows=rows)
         check_o(o[0, h], o_ref, rows, f"head {h}")
         check_lse(lse[0, h], l_ref, rows, f"head {h}")
-    del q, k, v, g, o, lse
+    del q, k, v, g, o, o16, lse, lse16
     torch.cuda.empty_cache()
 
 
@@ -1016,7 +1078,9 @@ def test_key_terms_last_key(kind, walk):
         dev_b = up(ref_b)
     ref = oracle.quantize_qk(q, k)
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, bias=ref_b, segments=segs)
-    o, l = qfa.attn_fwd(gpu_quant(q, k), up(v), w.sm_scale, bias=dev_b, segments=segs, return_lse=True)
+    g, tv = gpu_quant(q, k), up(v)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=dev_b, segments=segs, out_dtype=dt,
+                                                return_lse=True), tv.dtype, f"{kind} {walk}")
     check_o(o, o_ref, what=f"{kind} {walk}")
     check_lse(l, l_ref, what=f"{kind} {walk}")
 
@@ -1036,7 +1100,9 @@ def test_nan_rows_past_walked_ranges_never_read(splits):
     nan_bits = np.uint16(0x7FC0)   # bf16 quiet NaN
     vn[:, :, 100:128, :] = nan_bits
     vn[:, :, 227:, :] = nan_bits
-    o, l = qfa.attn_fwd(gpu_quant(q, k), up(vn), w.sm_scale, segments=segs, splits=splits, return_lse=True)
+    g, tvn = gpu_quant(q, k), up(vn)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tvn, w.sm_scale, segments=segs, splits=splits, out_dtype=dt,
+                                                return_lse=True), tvn.dtype, f"splits {splits}")
     check_o(o, o_ref, what=f"segments, splits {splits}")
     check_lse(l, l_ref, what=f"segments, splits {splits}")
 
@@ -1062,7 +1128,57 @@ def test_nan_pad_rows_block_sparse():
         x[:, :, pad, :] = np.uint16(0x7FC0)
     g = qfa.quantize_qk(up(qn), up(kn), up(vbs))
     idx, cnt = qfa.blockmask_to_index(up(mask))
-    o, l = qfa.attn_fwd(g, up(vn), w.sm_scale, index=idx, count=cnt, vbs=up(vbs), return_lse=True)
+    tvn, tvbs = up(vn), up(vbs)
+    o, l = both_outputs(lambda dt: qfa.attn_fwd(g, tvn, w.sm_scale, index=idx, count=cnt, vbs=tvbs, out_dtype=dt,
+                                                return_lse=True), tvn.dtype, "sparse pads NaN")
     valid_rows = np.flatnonzero(~np.tile(pad, H))
     check_o(o, o_ref[valid_rows], valid_rows, "sparse pads NaN")
     check_lse(l, l_ref[valid_rows], valid_rows, "sparse pads NaN")
+
+
+def test_quantize_non_finite_rows():
+    """Non-finite Q/K values: rows holding NaN or +-inf get codes 0, scale NaN (and a NaN centring
+    term for Q); an inf among a K channel's valid keys makes that channel's mean NaN, so every
+    centred row of that K/V head gets scale NaN; heads without one are unaffected. Bit-exact
+    against the oracle, NaN positions included, for bf16 and fp16."""
+    w = W.WORKLOADS["d64"]
+    for dt in ("bf16", "fp16"):
+        q, k, _ = W.make_qkv(w, B=1, H=4, Hkv=2, Sq=200, Sk=300)
+        qf, kf = W.to_f32(q), W.to_f32(k)
+        qf[0, 0, 3, 5] = np.nan
+        qf[0, 1, 7, 0] = np.inf
+        qf[0, 3, 199, 63] = -np.inf
+        kf[0, 1, 17, 9] = np.inf        # K/V head 1: mean of channel 9 is NaN
+        conv = W.f32_to_bf16_bits if dt == "bf16" else (lambda x: x.astype(np.float16))
+        q2, k2 = conv(qf), conv(kf)
+        g = gpu_quant(q2, k2)
+        ref = oracle.quantize_qk(q2, k2)
+        for name in ("q8", "qs", "k8", "ks", "kmean"):
+            a, b = down(g[name]), ref[name]
+            assert np.array_equal(a, b, equal_nan=a.dtype.kind == "f"), f"{dt} {name}"
+        # the centring term: NaN on the same rows, the finite ones within the usual bound
+        assert np.array_equal(np.isnan(down(g["qmu"])), np.isnan(ref["qmu"])), f"{dt} qmu"
+        assert np.isnan(ref["qs"][0, 0, 3]) and np.isnan(ref["qs"][0, 1, 7]) and np.isnan(ref["qs"][0, 3, 199])
+        assert np.all(np.isnan(ref["ks"][0, 1])) and np.all(np.isfinite(ref["ks"][0, 0]))
+        fin = np.isfinite(ref["qmu"])
+        assert np.max(np.abs(down(g["qmu"])[fin] - ref["qmu"][fin])) <= 1e-4 * max(1.0, np.abs(ref["qmu"][fin]).max())
+
+
+def test_debug_log_names_the_instance():
+    """QFA_DEBUG=1 prints one line per launch naming the kernel instance and its grid."""
+    import subprocess
+    import sys
+    code = ("import torch, quantized_flash_attention_amd as qfa\n"
+            "q = torch.randn(1, 2, 300, 128, device='cuda').to(torch.bfloat16)\n"
+            "g = qfa.quantize_qk(q, q)\n"
+            "qfa.attn_fwd(g, q, 0.088, return_lse=True, causal=True)\n"
+            "torch.cuda.synchronize()\n")
+    env = dict(os.environ, QFA_DEBUG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [x for x in r.stderr.splitlines() if x.startswith("qfa: ")]
+    assert any("kmean_partial_kernel<bf16, D=128>" in x for x in lines), lines
+    assert any("quantize_kernel<bf16, D=128>" in x for x in lines), lines
+    assert any("attn_fwd_kernel<D=128, V=bf16, sparse=0, bias=0, lse=1, causal=1, qk=int8" in x and "grid 6 x 256" in x
+               for x in lines), lines

@@ -159,3 +159,44 @@ def test_kmean_of_no_keys_is_zero(oracle_lib):
     assert np.array_equal(ref["qmu"], np.zeros((2, 3, 5)))
     kp = W.normal(1, 1, (1, 1, 64, 128), "bf16")
     assert np.array_equal(oracle_lib.kmean(kp, np.array([0], np.int32)), np.zeros((1, 1, 128), np.float32))
+
+
+def test_non_finite_rows(oracle_lib):
+    """The non-finite reading: a Q row holding NaN or +-inf quantizes to codes 0 with scale NaN and a
+    NaN centring term, its finite neighbours are unaffected; a K channel with an inf among its valid
+    keys has mean NaN, so every centred row of that head is such a row. A NaN in a pad row (vbs) is
+    never read. Hand-built rows, checked element by element."""
+    D = 8
+    q = np.zeros((1, 1, 4, D), np.float32)
+    q[0, 0, 0] = [1, -2, 3, -4, 5, -6, 7, -127]          # finite: codes are the values themselves
+    q[0, 0, 1] = [1, np.nan, 3, 4, 5, 6, 7, 8]
+    q[0, 0, 2] = [np.inf, 0, 0, 0, 0, 0, 0, 0]
+    q[0, 0, 3] = [-np.inf, np.nan, 1, 1, 1, 1, 1, 1]
+    k = np.zeros((1, 1, 3, D), np.float32)
+    k[0, 0, :, :] = [[1, 2, 3, 4, 5, 6, 7, 8], [2, 2, 2, 2, 2, 2, 2, 2], [0, 1, 0, 1, 0, 1, 0, 1]]
+    r = oracle_lib.quantize_qk(q, k)
+    assert r["q8"][0, 0, 0].tolist() == [1, -2, 3, -4, 5, -6, 7, -127] and r["qs"][0, 0, 0] == 1.0
+    for i in (1, 2, 3):
+        assert np.all(r["q8"][0, 0, i] == 0) and np.isnan(r["qs"][0, 0, i]) and np.isnan(r["qmu"][0, 0, i])
+    assert np.isfinite(r["qmu"][0, 0, 0]) and np.all(np.isfinite(r["kmean"]))
+    # K: an inf in channel 3 makes that channel's mean NaN and every centred row non-finite
+    k_bad = k.copy()
+    k_bad[0, 0, 1, 3] = np.inf
+    r = oracle_lib.quantize_qk(q[:, :, :1], k_bad)
+    mu = r["kmean"].reshape(-1)
+    assert np.isnan(mu[3]) and np.all(np.isfinite(np.delete(mu, 3)))
+    assert np.all(r["k8"] == 0) and np.all(np.isnan(r["ks"]))
+    assert np.isnan(r["qmu"][0, 0, 0])                      # q . mu meets the NaN channel
+    # uncentred, only the row holding the inf is affected
+    r = oracle_lib.quantize_qk(q[:, :, :1], k_bad, center_k=False)
+    assert np.isnan(r["ks"][0, 0, 1]) and np.all(r["k8"][0, 0, 1] == 0)
+    assert np.all(np.isfinite(r["ks"][0, 0, [0, 2]])) and r["k8"][0, 0, 0].tolist() == [16, 32, 48, 64, 79, 95, 111, 127]
+    # a NaN in a pad row of a vbs call is never read: same result as a zero there
+    kv = np.zeros((1, 1, 64, D), np.float32)
+    kv[0, 0, :5] = np.arange(40, dtype=np.float32).reshape(5, 8) - 20
+    kv_nan = kv.copy()
+    kv_nan[0, 0, 5:] = np.nan
+    vbs = np.array([5], np.int32)
+    a, b = oracle_lib.quantize_qk(kv, kv, vbs), oracle_lib.quantize_qk(kv_nan, kv_nan, vbs)
+    for name in ("q8", "qs", "k8", "ks", "kmean", "qmu"):
+        assert np.array_equal(a[name], b[name]), name
