@@ -264,6 +264,19 @@ def main() -> int:
         "device": device_info(dev),
     }
 
+    # the on-box MFMA ceiling of the same instruction mix (after the timed steps: it runs the
+    # matrix cores flat out and would heat the GPU before them)
+    try:
+        ceil = probe_mfma(dev, 0)
+        out["roofline"]["measured_mfma_ceiling"] = ceil
+        out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["tflops"], 4)
+        # the same MFMAs with the tile's softmax VALU work interleaved, with no memory, LDS or barrier
+        ideal = probe_mfma(dev, 3)
+        out["roofline"]["measured_compute_only_tile"] = ideal
+        out["roofline"]["frac_of_compute_only_tile"] = round(achieved / ideal["tflops"], 4)
+    except (OSError, RuntimeError) as e:
+        out["roofline"]["measured_mfma_ceiling"] = {"error": str(e)[:200]}
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -349,6 +362,70 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+PROBE_LIB = os.path.join(ROOT, "quantized_flash_attention_amd", "libqfa_probe.so")
+# multiply-add pairs counted as 2 ops each: one wave-iteration of the probe is one 32-row x 64-key
+# attention tile's MFMAs (8 int8 32x32x32 + 16 bf16 32x32x16)
+PROBE_OPS = {0: 8 * 65536 + 16 * 32768, 1: 8 * 65536, 2: 16 * 32768, 3: 8 * 65536 + 16 * 32768, 4: 0,
+             5: 16 * 32768, 6: 8 * 65536 + 16 * 32768}
+PROBE_PEAK = {0: PEAK_BLEND, 1: PEAK_I8_TOPS, 2: PEAK_BF16_TFLOPS, 3: PEAK_BLEND, 4: None, 5: PEAK_BF16_TFLOPS,
+              6: PEAK_BLEND}
+PROBE_MIX = ["int8 QK + bf16 PV MFMAs (attention tile)", "int8 32x32x32 only", "bf16 32x32x16 only",
+             "attention tile MFMAs + its softmax VALU work (64 fma, 16 max, 32 exp2, 16 pack, 16 dot2 per lane)",
+             "the softmax VALU work alone", "bf16 32x32x16 only, constant operands",
+             "int8 QK + bf16 PV MFMAs, constant operands"]
+
+
+def probe_mfma(dev, mix: int = 0, iters: int = 4000, reps: int = 3) -> dict:
+    """The matrix-core throughput the GPU sustains for the attention tile's MFMA mix (qfa_probe_mfma:
+    random operands, the attention kernel's launch shape of two 4-wave blocks per CU), with the
+    shader clock the loop ran at (s_memtime cycles over the 100 MHz s_memrealtime). Each launch runs
+    a few milliseconds: much longer launches of back-to-back MFMAs were seen to slow down about 30x
+    at a high reported clock, which measures a throttle, not the matrix cores."""
+    import ctypes
+
+    import torch
+
+    L = ctypes.CDLL(PROBE_LIB)
+    L.qfa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    L.qfa_probe_mfma.restype = ctypes.c_int
+    blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    sink = torch.empty(256 * blocks, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        st = L.qfa_probe_mfma(blocks, iters, mix, ctypes.c_void_p(clocks.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                              ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"qfa_probe_mfma returned {st}")
+
+    launch()
+    torch.cuda.synchronize()
+    times, clks = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        c = clocks.view(-1, 2).double().sum(0).tolist()
+        clks.append(c[0] / c[1] * 0.1)   # cycles per 10 ns tick -> GHz
+    ms = statistics.median(times)
+    ghz = statistics.median(clks)
+    ncu = blocks // 2
+    waves_per_simd = blocks * 4 / (4 * ncu)
+    out = {"mix": PROBE_MIX[mix], "clock_ghz": round(ghz, 3), "ms": round(ms, 3), "blocks": blocks, "iters": iters,
+           # SIMD cycles per wave-iteration: one iteration is one 32-row x 64-key tile of one wave
+           "simd_cycles_per_wave_tile": round(ms * 1e-3 * ghz * 1e9 / (iters * waves_per_simd), 1)}
+    if PROBE_OPS[mix]:
+        tflops = blocks * 4 * iters * PROBE_OPS[mix] / (ms * 1e-3) / 1e12
+        out.update(tflops=round(tflops, 1), frac_of_published_peak=round(tflops / PROBE_PEAK[mix], 4),
+                   frac_of_peak_at_this_clock=round(tflops / (PROBE_PEAK[mix] * ghz / 2.4), 4))
+    return out
+
+
 def device_info(dev) -> dict:
     import torch
 
@@ -396,6 +473,9 @@ def other_configs(dev) -> int:
         return B * H * (Sq + 2 * Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
 
     info = device_info(dev)
+    print(json.dumps({"config": "mfma_ceiling", "what": "qfa_probe_mfma: the attention tile's MFMA mix on random "
+                      "operands, 2 blocks of 4 waves per CU, no other work",
+                      "rows": [probe_mfma(dev, m) for m in range(7)], "device": info}), flush=True)
     for name in ("dense4k", "d64"):
         w = W.WORKLOADS[name]
         q_np, k_np, v_np = W.make_qkv(w)

@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build", "qfa")
 LIB = os.path.join(PKG, "libqfa.so")
+# the measurement helper (include/qfa_probe.h): its own library, not part of the attention ABI
+PROBE_SRC = "mfma_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libqfa_probe.so")
 
 # the attention kernel's instances are split over four translation units compiled in parallel
 ATTN_INST = ["attn_fwd_inst_d128_bf16.hip", "attn_fwd_inst_d128_fp16.hip", "attn_fwd_inst_d64_bf16.hip",
@@ -35,6 +38,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
 # the attention kernel's assembly is kept (-save-temps=obj) for the check below
 EXTRA = {src: ["-fno-honor-nans", "-save-temps=obj"] for src in ATTN_INST}
 EXTRA["attn_fwd.hip"] = ["-fno-honor-nans"]
+EXTRA["mfma_probe.hip"] = ["-fno-honor-nans", "-save-temps=obj"]
 ATTN_ASM = [os.path.join(BUILD, os.path.splitext(src)[0] + "-hip-amdgcn-amd-amdhsa-gfx950.s") for src in ATTN_INST]
 
 
@@ -50,8 +54,9 @@ def _compile(src: str) -> str:
 def build(jobs: int = 8) -> str:
     """Compile every source and link libqfa.so next to this file; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    probe_obj = objs.pop()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,6 +69,12 @@ def build(jobs: int = 8) -> str:
         os.remove(LIB) if os.path.exists(LIB) else None
         raise RuntimeError(f"bias-load registers used before their wait: {bad}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe_obj], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

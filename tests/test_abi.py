@@ -17,8 +17,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libqf
 FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(qfa_\w+)\(", text, re.M)))
 
 
@@ -30,6 +30,22 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, s), s
     assert L.qfa_version() >= 100
     assert L.qfa_status_string(2) == b"unsupported"
+
+
+def test_probe_library_exports_its_header():
+    """The measurement helper library (include/qfa_probe.h) loads and exports what its header declares;
+    its argument checks run on the host (no GPU call happens for a rejected argument)."""
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libqfa_probe.so")
+    L = ctypes.CDLL(path)
+    syms = declared_symbols(os.path.join(ROOT, "include", "qfa_probe.h"))
+    assert syms == ["qfa_probe_mfma"]
+    for s in syms:
+        assert hasattr(L, s), s
+    L.qfa_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    assert L.qfa_probe_mfma(0, 4, 0, FAKE, FAKE, None) == 1        # no blocks
+    assert L.qfa_probe_mfma(8, 6, 0, FAKE, FAKE, None) == 1        # iterations not a multiple of 4
+    assert L.qfa_probe_mfma(8, 4, 7, FAKE, FAKE, None) == 1        # no such mix
+    assert L.qfa_probe_mfma(8, 4, 0, None, FAKE, None) == 1
 
 
 def test_workspace_size():
