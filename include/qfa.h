@@ -126,6 +126,26 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, i
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qfa_quantize_qk_noalloc — qfa_quantize_qk without the workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The K-mean
+ * partials go to a scratch array of 8 MiB that the library holds in static
+ * device memory, one copy per GPU it runs on, until the process ends; the
+ * call allocates nothing. Arguments, outputs and errors as qfa_quantize_qk;
+ * in addition a centring call with B*Hkv above 4096 is rejected with
+ * QFA_ERR_UNSUPPORTED before any launch. The calls of a process on one GPU
+ * share its scratch, which keeps the last call's contents (nothing in it needs
+ * clearing: a call reads only what it wrote): calls that overlap in time on
+ * one GPU (different streams or threads) race; calls ordered on one stream do
+ * not.
+ */
+int qfa_quantize_qk_noalloc(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                            const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                            const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                            const int32_t* vbs, int center_k,
+                            int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu, void* stream);
+
+/*
  * qfa_blockmask_to_index — tile mask to per-query-tile key-tile lists
  * (FastVideo "minimax_h3_sparse_int8", sparse_sm89_attention: map_to_index).
  *

@@ -23,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import QFA_BF16, QFA_BOOL, QFA_FP16, QFA_FP32, QFAError
 
-__all__ = ["quantize_qk", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
+__all__ = ["quantize_qk", "quantize_qk_noalloc", "blockmask_to_index", "attn_fwd", "lse_merge", "int8_attention", "QFAError",
            "quantize_workspace_bytes", "qk_scores_i32", "split_workspace_bytes", "splits_auto", "attn_fwd_unquant"]
 
 _DT = {torch.bfloat16: QFA_BF16, torch.float16: QFA_FP16, torch.float32: QFA_FP32}
@@ -97,6 +97,39 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = Non
         _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(kmean), _ptr(qmu),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev)))
     return dict(q8=q8, qs=qs, k8=k8, ks=ks, kmean=kmean, qmu=qmu)
+
+
+def quantize_qk_noalloc(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = None, center_k: bool = True,
+                        out: dict | None = None) -> dict:
+    """:func:`quantize_qk` through qfa_quantize_qk_noalloc: the library allocates nothing (its K-mean
+    partials live in static device memory); the outputs are the tensors of ``out`` (keys q8, qs, k8,
+    ks, kmean, qmu as :func:`quantize_qk` returns them), allocated here only when it is None."""
+    _no_grad(q, k)
+    B, H, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or k.dtype != q.dtype:
+        raise ValueError("q and k must agree in B, D and dtype")
+    dq, *qst = _view(q, "q")
+    _, *kst = _view(k, "k")
+    dev = q.device
+    vbs = _cont(vbs, "vbs", torch.int32)
+    if out is None:
+        out = dict(q8=torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev),
+                   qs=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+                   k8=torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev),
+                   ks=torch.empty((B, Hkv, Sk), dtype=torch.float32, device=dev),
+                   kmean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if center_k else None,
+                   qmu=torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if center_k else None)
+    _shape(out["q8"], "q8", (B, H, Sq, D)), _shape(out["k8"], "k8", (B, Hkv, Sk, D))
+    _shape(out["qs"], "qs", (B, H, Sq)), _shape(out["ks"], "ks", (B, Hkv, Sk))
+    _cont(out["q8"], "q8", torch.int8), _cont(out["k8"], "k8", torch.int8)
+    _cont(out["qs"], "qs", torch.float32), _cont(out["ks"], "ks", torch.float32)
+    _cont(out.get("kmean"), "kmean", torch.float32), _cont(out.get("qmu"), "qmu", torch.float32)
+    _lib.check(_lib.lib().qfa_quantize_qk_noalloc(
+        B, H, Hkv, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
+        _ptr(out["q8"]), _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out.get("kmean")),
+        _ptr(out.get("qmu")), _stream(dev)))
+    return out
 
 
 def blockmask_to_index(mask: torch.Tensor):

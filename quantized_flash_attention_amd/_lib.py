@@ -21,6 +21,7 @@ EXPORTS = (
     "qfa_last_error",
     "qfa_quantize_workspace_bytes",
     "qfa_quantize_qk",
+    "qfa_quantize_qk_noalloc",
     "qfa_blockmask_to_index",
     "qfa_attn_fwd",
     "qfa_attn_fwd_splitk",
@@ -54,6 +55,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.qfa_quantize_qk.argtypes = ([_I64] * 6 + [_I] + [_P, _I64, _I64, _I64] * 2
                                   + [_P, _I] + [_P] * 6 + [_P, ctypes.c_size_t, _P])
     L.qfa_quantize_qk.restype = _I
+    L.qfa_quantize_qk_noalloc.argtypes = L.qfa_quantize_qk.argtypes[:-3] + [_P]
+    L.qfa_quantize_qk_noalloc.restype = _I
     L.qfa_blockmask_to_index.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P]
     L.qfa_blockmask_to_index.restype = _I
     # sm_scale, bias, block-sparse lists, v_scale, segments, causal, out, lse

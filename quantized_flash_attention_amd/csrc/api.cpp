@@ -186,6 +186,30 @@ int qfa_quantize_qk(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, i
                        q8, qs, k8, ks, kmean, qmu, workspace, workspace_bytes, stream);
 }
 
+int qfa_quantize_qk_noalloc(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int dtype,
+                            const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                            const void* k, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                            const int32_t* vbs, int center_k,
+                            int8_t* q8, float* qs, int8_t* k8, float* ks, float* kmean, float* qmu, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Sq, Sk, D))) return st;
+  if ((st = check_kv_heads(H, Hkv))) return st;
+  void* ws = nullptr;
+  size_t cap = 0;
+  const int64_t need = center_k ? qfa::quantize_workspace_size(B * Hkv, Sk, D) : 0;
+  if (need > 0) {
+    if (B * Hkv > qfa::kMeanSlots)
+      return fail(QFA_ERR_UNSUPPORTED, "qfa_quantize_qk_noalloc: the K-mean scratch holds %lld (batch, K/V head) "
+                  "pairs, the call has %lld", (long long)qfa::kMeanSlots, (long long)(B * Hkv));
+    if ((st = hip_status(qfa::noalloc_scratch(&ws, &cap), "scratch address"))) return st;
+    if ((size_t)need > cap)
+      return fail(QFA_ERR_UNSUPPORTED, "qfa_quantize_qk_noalloc: the call needs %lld bytes of scratch, %zu exist",
+                  (long long)need, cap);
+  }
+  return quantize_impl(B, H, Hkv, Sq, Sk, D, dtype, q, q_sb, q_sh, q_ss, k, k_sb, k_sh, k_ss, vbs, center_k,
+                       q8, qs, k8, ks, kmean, qmu, ws, cap, stream);
+}
+
 int qfa_blockmask_to_index(const uint8_t* mask, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
                            int32_t* index, int32_t* count, void* stream) {
   if (B < 0 || H < 0 || Tq < 0 || Tk < 0) return fail(QFA_ERR_INVALID_ARG, "negative size");

@@ -54,6 +54,8 @@ struct QuantArgs {
   void* workspace;                // quantize_workspace_size bytes (centring with Sk > 0)
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+// device address and size of this GPU's scratch for qfa_quantize_qk_noalloc
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 // Clears `words` 32-bit words with a fill kernel (never a memset node, so a
 // captured graph replays it faithfully).

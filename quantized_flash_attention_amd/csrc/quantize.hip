@@ -21,6 +21,8 @@
 
 #include <float.h>
 
+#include <mutex>
+
 namespace qfa {
 namespace {
 
@@ -294,6 +296,35 @@ hipError_t launch_dt_d(const QuantArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Scratch of qfa_quantize_qk_noalloc: the K-mean partials of a call, at most
+// kMeanSlots slots of up to 128 channels (8 MiB). Every slot a call reads was
+// written earlier in the same call, so nothing in it needs clearing; calls
+// that overlap on one GPU share it and race.
+constexpr size_t kNoAllocScratchBytes = (size_t)kMeanSlots * 128 * 16;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  // the device address of each GPU's copy of `scratch`, taken once per device
+  // with that device current (host code never uses the array's name itself)
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  *bytes = kNoAllocScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.D == 128) return a.dtype == BF16 ? launch_dt_d<BF16, 128>(a, s) : launch_dt_d<FP16, 128>(a, s);
