@@ -366,13 +366,18 @@ PROBE_LIB = os.path.join(ROOT, "quantized_flash_attention_amd", "libqfa_probe.so
 # multiply-add pairs counted as 2 ops each: one wave-iteration of the probe is one 32-row x 64-key
 # attention tile's MFMAs (8 int8 32x32x32 + 16 bf16 32x32x16)
 PROBE_OPS = {0: 8 * 65536 + 16 * 32768, 1: 8 * 65536, 2: 16 * 32768, 3: 8 * 65536 + 16 * 32768, 4: 0,
-             5: 16 * 32768, 6: 8 * 65536 + 16 * 32768}
+             5: 16 * 32768, 6: 8 * 65536 + 16 * 32768, 7: 8 * 65536 + 16 * 32768, 8: 8 * 65536 + 16 * 32768,
+             9: 8 * 65536 + 16 * 32768, 10: 8 * 65536 + 16 * 32768}
 PROBE_PEAK = {0: PEAK_BLEND, 1: PEAK_I8_TOPS, 2: PEAK_BF16_TFLOPS, 3: PEAK_BLEND, 4: None, 5: PEAK_BF16_TFLOPS,
-              6: PEAK_BLEND}
+              6: PEAK_BLEND, 7: PEAK_BLEND, 8: PEAK_BLEND, 9: PEAK_BLEND, 10: PEAK_BLEND}
 PROBE_MIX = ["int8 QK + bf16 PV MFMAs (attention tile)", "int8 32x32x32 only", "bf16 32x32x16 only",
              "attention tile MFMAs + its softmax VALU work (64 fma, 16 max, 32 exp2, 16 pack, 16 dot2 per lane)",
              "the softmax VALU work alone", "bf16 32x32x16 only, constant operands",
-             "int8 QK + bf16 PV MFMAs, constant operands"]
+             "int8 QK + bf16 PV MFMAs, constant operands",
+             "MFMA phase and VALU phase alternating between barriers, second wave group one phase behind",
+             "MFMA phase and VALU phase alternating between barriers, both wave groups in step",
+             "tile MFMAs + softmax VALU work, bf16 accumulators in AccVGPRs",
+             "tile MFMAs + softmax VALU work, every accumulator in AccVGPRs"]
 
 
 def probe_mfma(dev, mix: int = 0, iters: int = 4000, reps: int = 3) -> dict:
@@ -391,7 +396,7 @@ def probe_mfma(dev, mix: int = 0, iters: int = 4000, reps: int = 3) -> dict:
     L.qfa_probe_mfma.restype = ctypes.c_int
     blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
     clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
-    sink = torch.empty(256 * blocks, dtype=torch.float32, device=dev)
+    sink = torch.empty(256 * (blocks + 1), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def launch():
@@ -402,6 +407,7 @@ def probe_mfma(dev, mix: int = 0, iters: int = 4000, reps: int = 3) -> dict:
 
     launch()
     torch.cuda.synchronize()
+    nrec = blocks if mix < 7 else (blocks + 1) // 2   # blocks that wrote a clock record
     times, clks = [], []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -410,7 +416,7 @@ def probe_mfma(dev, mix: int = 0, iters: int = 4000, reps: int = 3) -> dict:
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
-        c = clocks.view(-1, 2).double().sum(0).tolist()
+        c = clocks.view(-1, 2)[:nrec].double().sum(0).tolist()
         clks.append(c[0] / c[1] * 0.1)   # cycles per 10 ns tick -> GHz
     ms = statistics.median(times)
     ghz = statistics.median(clks)
@@ -475,7 +481,7 @@ def other_configs(dev) -> int:
     info = device_info(dev)
     print(json.dumps({"config": "mfma_ceiling", "what": "qfa_probe_mfma: the attention tile's MFMA mix on random "
                       "operands, 2 blocks of 4 waves per CU, no other work",
-                      "rows": [probe_mfma(dev, m) for m in range(7)], "device": info}), flush=True)
+                      "rows": [probe_mfma(dev, m) for m in range(11)], "device": info}), flush=True)
     for name in ("dense4k", "d64"):
         w = W.WORKLOADS[name]
         q_np, k_np, v_np = W.make_qkv(w)

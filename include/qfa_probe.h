@@ -22,7 +22,15 @@ extern "C" {
  *   mix 3: mix 0 plus the tile's softmax VALU work (per lane: 64 fma, 16 max,
  *          32 exp2, 16 bf16 pack, 16 dot2) on independent registers;
  *   mix 4: that VALU work alone.
- *   mix 5: mix 2 and mix 6: mix 0, on constant operands (codes 1, values 1.0).
+ *   mix 5: mix 2 and mix 6: mix 0, on constant operands (codes 1, values 1.0);
+ *   mix 7: the tile's MFMAs and its VALU work in separate phases between
+ *          block barriers, blocks of 8 waves (blocks/2 launched, one per CU)
+ *          whose second 4-wave group runs one phase behind the first (each
+ *          SIMD then runs one wave's MFMA phase beside the other's VALU
+ *          phase); mix 8: the same with both groups in step.
+ *   sink then needs 512*ceil(blocks/2) floats;
+ *   mix 9: mix 3 with the bf16 MFMAs' accumulators in AccVGPRs;
+ *   mix 10: mix 3 with every accumulator in AccVGPRs.
  * Mixes 3 and 4 show how much of the VALU work the matrix-core time hides;
  * mixes 5 and 6 how much the operand data changes the sustained rate.
  * clocks: device buffer of 2*blocks uint64, written with (shader-clock
