@@ -44,7 +44,7 @@ def test_probe_library_exports_its_header():
     L.qfa_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
     assert L.qfa_probe_mfma(0, 4, 0, FAKE, FAKE, None) == 1        # no blocks
     assert L.qfa_probe_mfma(8, 6, 0, FAKE, FAKE, None) == 1        # iterations not a multiple of 4
-    assert L.qfa_probe_mfma(8, 4, 7, FAKE, FAKE, None) == 1        # no such mix
+    assert L.qfa_probe_mfma(8, 4, 11, FAKE, FAKE, None) == 1       # no such mix
     assert L.qfa_probe_mfma(8, 4, 0, None, FAKE, None) == 1
 
 
