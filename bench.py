@@ -287,7 +287,7 @@ def main() -> int:
 
     if args.cpu_baseline == "on":
         out["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, bias32_np, w, core, skirts, args.cpu_rows,
-                                           args.cpu_heads)
+                                           args.cpu_heads, gpu_ms=med)
 
     print(json.dumps(out))
     return 0
@@ -657,10 +657,43 @@ def other_configs(dev) -> int:
     return 0
 
 
-def cpu_baseline(q_np, k_np, v_np, bias_np, w, core, skirts, rows, heads=3):
-    """The oracle, as it stands, on a bounded sample: the first `heads` heads,
-    their first `rows` query rows against all 33600 keys, for the same step
-    (quantize, unmasked, fp32 bias, core + skirt + merge)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# the tiny configuration (B1 H2 S256 D128, K centred, LSE) through the oracle on one thread, best of 3;
+# run in a child process (OMP_NUM_THREADS=1 must be set before the OpenMP runtime starts) that
+# never touches the GPU
+_C1_SINGLE = """
+import json, sys, time
+sys.path.insert(0, %r)
+import oracle, workloads as W
+w = W.WORKLOADS["tiny"]
+q, k, v = W.make_qkv(w)
+best = None
+for _ in range(3):
+    t0 = time.perf_counter()
+    ref = oracle.quantize_qk(q, k)
+    oracle.attn(ref, v, w.sm_scale)
+    dt = time.perf_counter() - t0
+    best = dt if best is None else min(best, dt)
+print(json.dumps({"seconds": best}))
+"""
+
+
+def cpu_baseline(q_np, k_np, v_np, bias_np, w, core, skirts, rows, heads=3, gpu_ms=None):
+    """The oracle, as it stands, on a bounded sample: the first `heads` heads, their first `rows`
+    query rows against all 33600 keys, leg by leg as the GPU step runs them (quantize, unmasked,
+    fp32 bias, core + skirt + merge), with the oracle's bias/unmasked and split/single ratios beside
+    the GPU's; plus the tiny configuration on one thread."""
+    import subprocess
+
     import numpy as np
 
     import oracle
@@ -669,24 +702,50 @@ def cpu_baseline(q_np, k_np, v_np, bias_np, w, core, skirts, rows, heads=3):
     q1 = np.ascontiguousarray(q_np[:, :heads, :rows])
     k1 = np.ascontiguousarray(k_np[:, :heads])
     v1 = np.ascontiguousarray(v_np[:, :heads])
-    t0 = time.perf_counter()
-    ref = oracle.quantize_qk(q1, k1)
-    oracle.attn(ref, v1, w.sm_scale)
-    oracle.attn(ref, v1, w.sm_scale, bias=bias_np)
-    oc, lc = oracle.attn(ref, v1, w.sm_scale, segments=[core])
-    os_, ls = oracle.attn(ref, v1, w.sm_scale, bias=bias_np, segments=skirts)
-    oracle.lse_merge(oc, lc, os_, ls)
-    dt = time.perf_counter() - t0
+    legs = {}
+
+    def leg(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        legs[name] = time.perf_counter() - t0
+        return r
+
+    ref = leg("quantize", lambda: oracle.quantize_qk(q1, k1))
+    leg("unmasked", lambda: oracle.attn(ref, v1, w.sm_scale))
+    leg("bias_fp32", lambda: oracle.attn(ref, v1, w.sm_scale, bias=bias_np))
+    oc, lc = leg("core", lambda: oracle.attn(ref, v1, w.sm_scale, segments=[core]))
+    os_, ls = leg("skirt", lambda: oracle.attn(ref, v1, w.sm_scale, bias=bias_np, segments=skirts))
+    leg("merge", lambda: oracle.lse_merge(oc, lc, os_, ls))
+    dt = sum(legs.values())
     flops = 3 * 4.0 * heads * rows * w.Sk * w.D
-    return {
+    split = legs["core"] + legs["skirt"] + legs["merge"]
+    out = {
         "value": round(flops / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"heads 0..{heads - 1} of 56, query rows 0..{rows - 1} of 4096, all 33600 keys: K mean + int8 "
                   f"quantize, unmasked, fp32-bias, core+skirt+merge (same step); {dt:.1f} s",
         "seconds": round(dt, 2),
+        "leg_ms": {k: round(v * 1e3, 1) for k, v in legs.items()},
+        "oracle_bias_over_unmasked": round(legs["bias_fp32"] / legs["unmasked"], 3),
+        "oracle_split_over_single_bias": round(split / legs["bias_fp32"], 3),
     }
+    if gpu_ms:
+        out["gpu_bias_over_unmasked"] = round(gpu_ms["bias_fp32"] / gpu_ms["unmasked"], 3)
+        out["gpu_split_over_single_bias"] = round((gpu_ms["core"] + gpu_ms["skirt"] + gpu_ms["merge"])
+                                                  / gpu_ms["bias_fp32"], 3)
+    try:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", _C1_SINGLE % ROOT], env=env, capture_output=True, text=True,
+                           timeout=120)
+        c1 = json.loads(r.stdout.strip().splitlines()[-1])["seconds"]
+        out["tiny_single_thread"] = {"config": "B1 H2 S256 D128 bf16, K centred: quantize + attention, best of 3",
+                                     "ms": round(c1 * 1e3, 2), "threads": 1}
+    except (subprocess.SubprocessError, ValueError, IndexError) as e:
+        out["tiny_single_thread"] = {"error": str(e)[:200]}
+    return out
 
 
 if __name__ == "__main__":
