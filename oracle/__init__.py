@@ -24,7 +24,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# QFA_ORACLE_LIB names another build of oracle.c (the sanitizer test loads one built with ASan/UBSan)
+_LIB = os.environ.get("QFA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 BF16, FP16, FP32 = 1, 2, 3
 

@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqfa.so")
+# QFA_LIB_PATH names another build of the same library (the sanitizer test loads one whose host
+# code is built with ASan/UBSan); there is no other implementation to fall back to
+LIB_PATH = os.environ.get("QFA_LIB_PATH") or os.path.join(_HERE, "libqfa.so")
 
 QFA_OK, QFA_ERR_INVALID_ARG, QFA_ERR_UNSUPPORTED, QFA_ERR_HIP = 0, 1, 2, 3
 QFA_BF16, QFA_FP16, QFA_FP32, QFA_BOOL = 1, 2, 3, 4
