@@ -63,6 +63,15 @@ __device__ __forceinline__ bool is_pad(const int32_t* vbs, int64_t j) {
 // rows; block: 256 threads = D/8 channel groups x (2048/D) row slots, each
 // slot loading 4 rows at a time. The block's exact column sums go to its
 // partial slot.
+//
+// Each lane sums its values of a channel in plain fp64, which is exact when
+// every partial sum is representable: fp16 values are multiples of 2^-24 below
+// 2^16, so any sum of fewer than 2^13 of them is; a lane of bf16 values tracks
+// its largest and smallest nonzero magnitude, and the sum is exact when
+// (exponent span) + 8 significand bits + log2(values summed) <= 53, as every
+// value is then a multiple of the smallest one's ulp. A lane whose bf16 values
+// span more (tiny values beside large ones, subnormals) sums its rows again in
+// double-double. The slots' sums are combined in double-double.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nchunks, int64_t chunk_rows) {
   constexpr int G = D / 8;          // lanes per row
@@ -78,9 +87,13 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nch
   const int64_t r1 = min(r0 + chunk_rows, a.Sk);
   const uint16_t* base = (const uint16_t*)a.k + b * a.k_sb + h * a.k_sh + cg * 8;
 
-  DD acc[8];
+  double fsum[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = DD{0.0, 0.0};
+  for (int i = 0; i < 8; ++i) fsum[i] = 0.0;
+  // bf16: largest magnitude, and smallest nonzero magnitude minus one (as
+  // unsigned bits, so a zero wraps to the top and never counts)
+  uint32_t amax = 0u, amin_m1 = 0xffffffffu;
+  int64_t nvals = 0;   // values this lane adds per channel
   for (int64_t j = r0 + rs; j < r1; j += RP * U) {
     uint4 w[U];
 #pragma unroll
@@ -89,10 +102,45 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nch
       const bool live = jj < r1 && !is_pad(a.vbs, jj);
       w[u] = live ? *(const uint4*)(base + jj * a.k_ss) : make_uint4(0u, 0u, 0u, 0u);
     }
+    nvals += U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float f[8];
       unpack8<DT>(w[u], f);   // a skipped row adds exact zeros
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        fsum[i] += (double)f[i];
+        if (DT == BF16) {
+          const uint32_t m = __float_as_uint(f[i]) & 0x7fffffffu;
+          amax = max(amax, m);
+          amin_m1 = min(amin_m1, m - 1u);
+        }
+      }
+    }
+  }
+  bool exact = true;
+  if (DT == BF16 && amax != 0u) {
+    // exponents of the extreme magnitudes (a subnormal counts as 2^-149,
+    // which always fails the test below)
+    const int emax = (int)(amax >> 23) - 127;
+    const uint32_t amin = amin_m1 + 1u;
+    const int emin = (amin >> 23) == 0u ? -149 : (int)(amin >> 23) - 127;
+    const int lgn = 64 - __clzll((unsigned long long)max(nvals, (int64_t)1));   // > log2(nvals)
+    exact = emax - emin + 8 + lgn <= 53;
+  }
+  DD acc[8];
+  if (exact) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = DD{fsum[i], 0.0};
+  } else {
+    // the same rows again, summed in double-double
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = DD{0.0, 0.0};
+    for (int64_t j = r0 + rs; j < r1; j += RP) {
+      const bool live = !is_pad(a.vbs, j);
+      const uint4 w = live ? *(const uint4*)(base + j * a.k_ss) : make_uint4(0u, 0u, 0u, 0u);
+      float f[8];
+      unpack8<DT>(w, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i].add((double)f[i]);
     }

@@ -1182,3 +1182,29 @@ def test_debug_log_names_the_instance():
     assert any("quantize_kernel<bf16, D=128>" in x for x in lines), lines
     assert any("attn_fwd_kernel<D=128, V=bf16, sparse=0, bias=0, lse=1, causal=1, qk=int8" in x and "grid 6 x 256" in x
                for x in lines), lines
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_kmean_wide_exponent_spans(dtype):
+    """K-mean exactness where a plain fp64 sum would round: channels mixing values near 2^30 (bf16) or
+    6e4 (fp16) with values near 2^-60 (bf16) or subnormal fp16, exact zeros and a bf16 subnormal, in
+    chunks of several hundred rows; the kernel's double-double path for such lanes must reproduce the
+    oracle's exact mean bit for bit."""
+    w = W.WORKLOADS["dense4k"]
+    q, k, _ = W.make_qkv(w, H=3, Sq=64, Sk=3000)
+    kf = W.to_f32(k)
+    rs = np.random.default_rng(31)
+    if dtype == "bf16":
+        kf[0, 0, ::7, 3] *= np.float32(2.0 ** 30)
+        kf[0, 0, 1::7, 3] *= np.float32(2.0 ** -60)
+        kf[0, 1, :, 5] = 0.0
+        kf[0, 1, 17, 5] = np.float32(2.0 ** -130)          # a subnormal
+        kf[0, 2, rs.integers(0, 3000, 40), 9] *= np.float32(2.0 ** -40)
+        k2, q2 = W.f32_to_bf16_bits(kf), q
+    else:
+        kf[0, 0, ::7, 3] = 60000.0
+        kf[0, 0, 1::7, 3] = np.float32(2.0 ** -24)          # the smallest fp16 subnormal
+        kf[0, 1, :, 5] = 0.0
+        k2, q2 = kf.astype(np.float16), W.to_f32(q).astype(np.float16)
+    g = gpu_quant(q2, k2)
+    assert_quant_equal(g, oracle.quantize_qk(q2, k2))
