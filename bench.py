@@ -45,6 +45,9 @@ ATTN_SRC = sorted(os.path.join(ROOT, "quantized_flash_attention_amd", "csrc", f)
                   for f in os.listdir(os.path.join(ROOT, "quantized_flash_attention_amd", "csrc"))
                   if f.startswith("attn_fwd"))
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_band_unmasked_pmc.json")
+# the bandwidth kernels' sources (quantize, LSE merge, map-to-index)
+BW_SRC = [os.path.join(ROOT, "quantized_flash_attention_amd", "csrc", f)
+          for f in ("quantize.hip", "lse_merge.hip", "blockmask.hip")]
 
 
 def src_hash(paths) -> str:
@@ -81,10 +84,20 @@ def main() -> int:
     ap.add_argument("--configs", action="store_true",
                     help="instead of the step: time the other configurations (dense 4k with LSE off/on, d64 fp16, "
                          "tile-64 block-sparse 128k) and a bf16 / int8 GEMM on the box; one JSON line each")
+    ap.add_argument("--bandwidth", action="store_true",
+                    help="instead of the step: the bandwidth-bound calls (quantize, LSE merge, map-to-index) over "
+                         "rotated input sets larger than the MALL; one JSON line")
+    ap.add_argument("--only", default=None,
+                    help="with --configs or --bandwidth: comma-separated names of the lines/rows to run")
+    ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                    help="print a markdown table of rocprofv3 --pmc output directories (median per kernel and grid)")
+    ap.add_argument("--kernel", default=None, help="with --pmc-table: regular expression the kernel name must match")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE passes over "
                          "this script with --copy-calibration) into " + os.path.relpath(PMC_FILE, ROOT))
     args = ap.parse_args()
+    if args.pmc_table:
+        return pmc_table(args.pmc_table, args.kernel)
     if args.pmc_summary:
         return pmc_summary(*args.pmc_summary)
 
@@ -105,7 +118,9 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     if args.configs:
-        return other_configs(dev)
+        return other_configs(dev, args.only)
+    if args.bandwidth:
+        return bandwidth(dev, args.only)
     w = W.WORKLOADS["band"]
     B, H, Sq, Sk, D = w.B, w.H, w.Sq, w.Sk, w.D
     core, skirt = w.extras["core"], w.extras["skirt"]
@@ -194,10 +209,12 @@ def main() -> int:
     flops_full = 4.0 * B * H * Sq * Sk * D
     tflops = lambda fl, ms: fl / (ms * 1e-3) / 1e12
     split_ms = med["core"] + med["skirt"] + med["merge"]
-    # algorithmic bytes of the quantize step: read K twice (the mean, then the codes) and Q once,
-    # write codes, scales, mean, centring term
-    qbytes = (B * H * (Sq + 2 * Sk) * D * 2 + B * H * (Sq + Sk) * D + B * H * (Sq + Sk) * 4
+    # algorithmic bytes of the quantize step: read Q and K once, write codes, scales, mean,
+    # centring term (820 MB); the kernel's second read of K (the mean, then the codes) is
+    # implementation traffic, reported beside it
+    qbytes = (B * H * (Sq + Sk) * D * 2 + B * H * (Sq + Sk) * D + B * H * (Sq + Sk) * 4
               + B * H * D * 4 + B * H * Sq * 4)
+    qbytes_k2 = B * H * Sk * D * 2
     mbytes = B * H * Sq * (2 * D * 4 + 2 * 4 + D * 2 + 4)
     step_flops = 3 * flops_full
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -244,6 +261,9 @@ def main() -> int:
         "calls": {
             "quantize_ms": round(med["quantize"], 4),
             "quantize_GBps": round(qbytes / (med["quantize"] * 1e-3) / 1e9, 1),
+            "quantize_model_MB": round(qbytes / 1e6, 1),
+            "quantize_second_k_read_MB": round(qbytes_k2 / 1e6, 1),
+            "quantize_GBps_with_second_k_read": round((qbytes + qbytes_k2) / (med["quantize"] * 1e-3) / 1e9, 1),
             "unmasked_ms": round(med["unmasked"], 4),
             "unmasked_tflops": round(tflops(flops_full, med["unmasked"]), 1),
             "bias_fp32_ms": round(med["bias_fp32"], 4),
@@ -338,13 +358,22 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> int:
             raise SystemExit(f"no dispatch of {needle!r} in the counter files")
         return statistics.median(vals)
 
-    copy_f, copy_w = pick(fetch, "copyBuffer") * 1024.0, pick(write, "copyBuffer") * 1024.0
+    def pick_copy(d):
+        # the calibration copy: copyBuffer dispatches that moved at least a quarter of COPY_BYTES
+        # (torch's small device-to-device copies use the same kernel)
+        vals = [v for n, vs in d.items() if "copyBuffer" in n for v in vs if v * 1024.0 >= COPY_BYTES / 8]
+        if not vals:
+            raise SystemExit("no calibration copy in the counter files (run with --copy-calibration)")
+        return statistics.median(vals)
+
+    copy_f, copy_w = pick_copy(fetch) * 1024.0, pick_copy(write) * 1024.0
     f_scale, w_scale = COPY_BYTES / copy_f, COPY_BYTES / copy_w
     un_f, un_w = pick(fetch, UNMASKED_KERNEL) * 1024.0 * f_scale, pick(write, UNMASKED_KERNEL) * 1024.0 * w_scale
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py --cpu-baseline off "
            "--steps 2 --warmup 1 --variant-iters 1 --copy-calibration")
     out = {
-        "what": "HBM bytes per launch of the unmasked banded attention call (B1 H56 Sq4096 Sk33600 D128 bf16)",
+        "what": "HBM bytes per launch of the unmasked banded attention call (B1 H56 Sq4096 Sk33600 D128 bf16), "
+                "and of the step's quantize and LSE-merge kernels on the same workload",
         "kernel": UNMASKED_KERNEL,
         "source_sha256_16": src_hash(ATTN_SRC),
         "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
@@ -354,11 +383,72 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> int:
         "launches": {"unmasked": {"fetch_bytes": round(un_f), "write_bytes": round(un_w),
                                   "hbm_bytes_per_launch": round(un_f + un_w)}},
     }
+    # the step's bandwidth kernels on the same workload: the three launches of the quantize call
+    # and the LSE merge (same scaling), beside their algorithmic bytes
+    B, H, Sq, Sk, D = 1, 56, 4096, 33600, 128
+    q_model = (B * H * (Sq + Sk) * D * 2 + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4)
+    m_model = B * H * Sq * (2 * D * 4 + 2 * 4 + D * 2 + 4)
+    other = {}
+    for key, name in (("kmean_partial", "kmean_partial_kernel<1, 128>"), ("kmean_finalize", "kmean_finalize_kernel"),
+                      ("quantize", "quantize_kernel<1, 128>"), ("lse_merge", "lse_merge_kernel<128>")):
+        f_b, w_b = pick(fetch, name) * 1024.0 * f_scale, pick(write, name) * 1024.0 * w_scale
+        other[key] = {"kernel": name, "fetch_bytes": round(f_b), "write_bytes": round(w_b)}
+    qsum = sum(other[k]["fetch_bytes"] + other[k]["write_bytes"] for k in ("kmean_partial", "kmean_finalize", "quantize"))
+    out["bandwidth_kernels"] = {
+        "source_sha256_16": src_hash(BW_SRC),
+        "per_dispatch": other,
+        "quantize_call": {"hbm_bytes": qsum, "algorithmic_bytes": q_model,
+                          "second_k_read_bytes": B * H * Sk * D * 2,
+                          "ratio_to_algorithmic": round(qsum / q_model, 3)},
+        "lse_merge": {"hbm_bytes": other["lse_merge"]["fetch_bytes"] + other["lse_merge"]["write_bytes"],
+                      "algorithmic_bytes": m_model},
+    }
     os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
     with open(PMC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(json.dumps(out["launches"]["unmasked"]))
+    return 0
+
+
+def pmc_table(dirs, kernel_rx=None) -> int:
+    """Markdown table of rocprofv3 --pmc output directories: per kernel (and grid size), the number
+    of dispatches, their median duration and the median over dispatches of each counter (summed
+    over the rows a dispatch reports). FETCH_SIZE / WRITE_SIZE are printed in KiB as counted."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    rx = re.compile(kernel_rx) if kernel_rx else None
+    per = collections.defaultdict(lambda: collections.defaultdict(float))   # (dir, dispatch) -> counter -> value
+    meta = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("qfa::", "")
+                name = name.split("(")[0].replace("void ", "")
+                if rx and not rx.search(name):
+                    continue
+                key = (f, r["Dispatch_Id"])
+                per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                meta[key] = (name, int(r["Grid_Size"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    groups = collections.defaultdict(list)
+    for key, (name, grid, us) in meta.items():
+        groups[(name, grid)].append(key)
+    counters = sorted({c for v in per.values() for c in v})
+    print("| kernel | grid | dispatches | median us | " + " | ".join(counters) + " |")
+    print("|---|---:|---:|---:|" + "---:|" * len(counters))
+    for (name, grid), keys in sorted(groups.items()):
+        us = statistics.median(meta[k][2] for k in keys)
+        vals = []
+        for c in counters:
+            xs = [per[k][c] for k in keys if c in per[k]]
+            vals.append(f"{statistics.median(xs):.4g}" if xs else "")
+        print(f"| `{name}` | {grid} | {len(keys)} | {us:.1f} | " + " | ".join(vals) + " |")
     return 0
 
 
@@ -457,7 +547,7 @@ def _time_ms(fn, iters: int, warmup: int = 3) -> float:
     return statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
 
 
-def other_configs(dev) -> int:
+def other_configs(dev, only=None) -> int:
     """One JSON line per configuration besides the step's banded workload: quantize and attention
     times, effective TFLOPS (4*B*H*Sq*Sk_eff*D; block-sparse counts the selected 64x64 tile pairs,
     causal the S(S+1)/2 attended pairs)
@@ -475,14 +565,28 @@ def other_configs(dev) -> int:
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     def qbytes(B, H, Sq, Sk, D, esz):
-        # read K twice (the mean, then the codes) and Q once; write codes, scales, K mean, centring term
-        return B * H * (Sq + 2 * Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
+        # algorithmic bytes: read Q and K once; write codes, scales, K mean, centring term (the
+        # kernel's second read of K is implementation traffic). These lines re-quantize the same
+        # tensors, which the 256 MB MALL may hold: the HBM figures are those of --bandwidth.
+        return B * H * (Sq + Sk) * D * esz + B * H * (Sq + Sk) * (D + 4) + B * H * D * 4 + B * H * Sq * 4
+
+    names = ("mfma_ceiling", "dense4k", "d64", "dense4k_bias_forms", "flydsl_causal_shapes", "band_shard_h7_split_k",
+             "band_keep_mask", "sparse", "gemm_reference")
+    want = set(only.split(",")) if only else set(names)
+    if want - set(names):
+        print(f"bench.py: unknown --only lines {sorted(want - set(names))}; known: {', '.join(names)}", file=sys.stderr)
+        return 2
+
+    def sel(name):
+        return name in want
 
     info = device_info(dev)
-    print(json.dumps({"config": "mfma_ceiling", "what": "qfa_probe_mfma: the attention tile's MFMA mix on random "
-                      "operands, 2 blocks of 4 waves per CU, no other work",
-                      "rows": [probe_mfma(dev, m) for m in range(11)], "device": info}), flush=True)
-    for name in ("dense4k", "d64"):
+    if sel("mfma_ceiling"):
+        print(json.dumps({"config": "mfma_ceiling", "what": "qfa_probe_mfma: the attention tile's MFMA mix on random "
+                          "operands, 2 blocks of 4 waves per CU, no other work",
+                          "rows": [probe_mfma(dev, m) for m in range(11)], "device": info}), flush=True)
+
+    for name in [n for n in ("dense4k", "d64") if sel(n)]:
         w = W.WORKLOADS[name]
         q_np, k_np, v_np = W.make_qkv(w)
         q, k, v = up(q_np), up(k_np), up(v_np)
@@ -509,151 +613,316 @@ def other_configs(dev) -> int:
         del q, k, v, qk, out, lse, ws
         torch.cuda.empty_cache()
 
-    # dense4k with a materialised per-query bias [1,1,Q,K] (the slow path) against the shared
-    # per-key bias [1,1,1,K] and no bias
-    w = W.WORKLOADS["dense4k"]
-    q_np, k_np, v_np = W.make_qkv(w)
-    q, k, v = up(q_np), up(k_np), up(v_np)
-    qk = qfa.quantize_qk(q, k)
-    out = torch.empty_like(q)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(2)
-    b_key = torch.randn((1, 1, 1, w.Sk), generator=gen, device=dev)
-    b_f32 = torch.randn((1, 1, w.Sq, w.Sk), generator=gen, device=dev)
-    b_bf16 = b_f32.to(torch.bfloat16)
-    b_bool = b_f32 > -1.0
-    line = {"config": "dense4k_bias_forms", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} bf16"}
-    for name, b in (("none", None), ("per_key_fp32", b_key), ("per_query_fp32", b_f32),
-                    ("per_query_bf16", b_bf16), ("per_query_bool", b_bool)):
-        line[name + "_ms"] = round(_time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=b, out=out), 20), 4)
-    line["device"] = info
-    print(json.dumps(line), flush=True)
-    del q, k, v, qk, out, b_key, b_f32, b_bf16, b_bool
-    torch.cuda.empty_cache()
+    if sel("dense4k_bias_forms"):
+        # dense4k with a materialised per-query bias [1,1,Q,K] (the slow path) against the shared
+        # per-key bias [1,1,1,K] and no bias
+        w = W.WORKLOADS["dense4k"]
+        q_np, k_np, v_np = W.make_qkv(w)
+        q, k, v = up(q_np), up(k_np), up(v_np)
+        qk = qfa.quantize_qk(q, k)
+        out = torch.empty_like(q)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2)
+        b_key = torch.randn((1, 1, 1, w.Sk), generator=gen, device=dev)
+        b_f32 = torch.randn((1, 1, w.Sq, w.Sk), generator=gen, device=dev)
+        b_bf16 = b_f32.to(torch.bfloat16)
+        b_bool = b_f32 > -1.0
+        line = {"config": "dense4k_bias_forms", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} bf16"}
+        for name, b in (("none", None), ("per_key_fp32", b_key), ("per_query_fp32", b_f32),
+                        ("per_query_bf16", b_bf16), ("per_query_bool", b_bool)):
+            line[name + "_ms"] = round(_time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=b, out=out), 20), 4)
+        line["device"] = info
+        print(json.dumps(line), flush=True)
+        del q, k, v, qk, out, b_key, b_f32, b_bf16, b_bool
+        torch.cuda.empty_cache()
 
-    # the causal shapes of ROCm/FlyDSL PR #886's timed table, (B, S, H, Hkv, D) and its FlyDSL
-    # +LSE latency in us (bf16 QK on an MI350X: context, not a target); TFLOPS as that table
-    # counts them, half of 4*B*H*S*S*D
-    flydsl = [((2, 2048, 16, 16, 128), 51.3), ((2, 4096, 16, 16, 128), 154.7), ((1, 8192, 16, 16, 128), 262.8),
-              ((2, 2048, 16, 2, 128), 50.4), ((4, 2048, 8, 8, 64), 38.7), ((8, 1024, 16, 16, 128), 58.5)]
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(886)
-    rows = []
-    for (B, S, H, Hkv, D), page_us in flydsl:
-        q = torch.randn((B, H, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        k = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        v = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
-        ws = torch.empty(qfa.quantize_workspace_bytes(B, Hkv, S, D), dtype=torch.uint8, device=dev)
+    if sel("flydsl_causal_shapes"):
+        # the causal shapes of ROCm/FlyDSL PR #886's timed table, (B, S, H, Hkv, D) and its FlyDSL
+        # +LSE latency in us (bf16 QK on an MI350X: context, not a target); TFLOPS as that table
+        # counts them, half of 4*B*H*S*S*D
+        flydsl = [((2, 2048, 16, 16, 128), 51.3), ((2, 4096, 16, 16, 128), 154.7), ((1, 8192, 16, 16, 128), 262.8),
+                  ((2, 2048, 16, 2, 128), 50.4), ((4, 2048, 8, 8, 64), 38.7), ((8, 1024, 16, 16, 128), 58.5)]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(886)
+        rows = []
+        for (B, S, H, Hkv, D), page_us in flydsl:
+            q = torch.randn((B, H, S, D), generator=gen, device=dev).to(torch.bfloat16)
+            k = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn((B, Hkv, S, D), generator=gen, device=dev).to(torch.bfloat16)
+            ws = torch.empty(qfa.quantize_workspace_bytes(B, Hkv, S, D), dtype=torch.uint8, device=dev)
+            qk = qfa.quantize_qk(q, k, workspace=ws)
+            out = torch.empty_like(q)
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+            scale = D ** -0.5
+            t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
+            t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, scale, causal=True, out=out, lse=lse), 20)
+            t_b = _time_ms(lambda: qfa.attn_fwd_unquant(q, k, v, scale, causal=True, out=out, lse=lse), 20)
+            fl = 4.0 * B * H * S * S * D / 2
+            rows.append({"shape": f"B{B} S{S} H{H} Hkv{Hkv} D{D}", "quantize_us": round(t_q * 1e3, 1),
+                         "attn_us": round(t_a * 1e3, 1), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
+                         "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
+                         "end_to_end_us": round((t_q + t_a) * 1e3, 1),
+                         "bf16qk_us": round(t_b * 1e3, 1), "bf16qk_tflops": round(fl / (t_b * 1e-3) / 1e12, 1),
+                         "page_flydsl_lse_us": page_us})
+            del q, k, v, ws, qk, out, lse
+        torch.cuda.empty_cache()
+        print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V; int8 QK, and bf16 QK (bf16qk_*)",
+                          "rows": rows, "device": info}), flush=True)
+
+    if sel("band_shard_h7_split_k"):
+        # split-K on the banded workload's 8-GPU shard: 7 heads give 224 query blocks for 256 CUs
+        w = W.WORKLOADS["band"]
+        q_np, k_np, v_np = W.make_qkv(w, H=7)
+        q, k, v = up(q_np), up(k_np), up(v_np)
+        del q_np, k_np, v_np
+        bias = up(W.bias_tensor(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]), "fp32"))
+        qk = qfa.quantize_qk(q, k)
+        out = torch.empty_like(q)
+        lse = torch.empty((1, 7, w.Sq), dtype=torch.float32, device=dev)
+        ns = qfa.splits_auto(1, 7, w.Sq, w.Sk)
+        ws = torch.empty(max(1, qfa.split_workspace_bytes(1, 7, w.Sq, w.D, ns)), dtype=torch.uint8, device=dev)
+        line = {"config": "band_shard_h7_split_k", "shape": f"B1 H7 Sq{w.Sq} Sk{w.Sk} D{w.D} bf16, fp32 bias, LSE on",
+                "auto_splits": ns}
+        fl = 4.0 * 7 * w.Sq * w.Sk * w.D
+        for n in sorted({1, 2, ns, 8}):
+            wsn = ws if n == ns else None
+            t = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=bias, out=out, lse=lse, splits=n, workspace=wsn), 10)
+            line[f"splits{n}_ms"] = round(t, 4)
+            line[f"splits{n}_frac_blend"] = round(fl / (t * 1e-3) / 1e12 / PEAK_BLEND, 4)
+        line["device"] = info
+        print(json.dumps(line), flush=True)
+        del q, k, v, bias, qk, out, lse, ws
+        torch.cuda.empty_cache()
+
+    if sel("band_keep_mask"):
+        # the banded workload with the pages' bool [1,1,1,K] keep mask (raised-cosine weight > 1e-3)
+        w = W.WORKLOADS["band"]
+        q_np, k_np, v_np = W.make_qkv(w)
+        q, k, v = up(q_np), up(k_np), up(v_np)
+        del q_np, k_np, v_np
+        weights = np.exp(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]))
+        keep = torch.from_numpy((weights > 1e-3).reshape(1, 1, 1, -1)).to(dev)
+        ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
         qk = qfa.quantize_qk(q, k, workspace=ws)
         out = torch.empty_like(q)
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
-        scale = D ** -0.5
-        t_q = _time_ms(lambda: qfa.quantize_qk(q, k, workspace=ws), 20)
-        t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, scale, causal=True, out=out, lse=lse), 20)
-        t_b = _time_ms(lambda: qfa.attn_fwd_unquant(q, k, v, scale, causal=True, out=out, lse=lse), 20)
-        fl = 4.0 * B * H * S * S * D / 2
-        rows.append({"shape": f"B{B} S{S} H{H} Hkv{Hkv} D{D}", "quantize_us": round(t_q * 1e3, 1),
-                     "attn_us": round(t_a * 1e3, 1), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
-                     "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
-                     "end_to_end_us": round((t_q + t_a) * 1e3, 1),
-                     "bf16qk_us": round(t_b * 1e3, 1), "bf16qk_tflops": round(fl / (t_b * 1e-3) / 1e12, 1),
-                     "page_flydsl_lse_us": page_us})
-        del q, k, v, ws, qk, out, lse
-    torch.cuda.empty_cache()
-    print(json.dumps({"config": "flydsl_causal_shapes", "mode": "causal, LSE on, bf16 V; int8 QK, and bf16 QK (bf16qk_*)",
-                      "rows": rows, "device": info}), flush=True)
+        t_u = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out), 10)
+        t_k = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=keep, out=out), 10)
+        print(json.dumps({
+            "config": "band_keep_mask", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} {w.dtype}",
+            "kept_keys": int(keep.sum().item()), "unmasked_ms": round(t_u, 4), "keep_mask_ms": round(t_k, 4),
+            "keep_over_unmasked": round(t_k / t_u, 3), "device": info}), flush=True)
+        del q, k, v, qk, out, keep, ws
+        torch.cuda.empty_cache()
 
-    # split-K on the banded workload's 8-GPU shard: 7 heads give 224 query blocks for 256 CUs
-    w = W.WORKLOADS["band"]
-    q_np, k_np, v_np = W.make_qkv(w, H=7)
-    q, k, v = up(q_np), up(k_np), up(v_np)
-    del q_np, k_np, v_np
-    bias = up(W.bias_tensor(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]), "fp32"))
-    qk = qfa.quantize_qk(q, k)
-    out = torch.empty_like(q)
-    lse = torch.empty((1, 7, w.Sq), dtype=torch.float32, device=dev)
-    ns = qfa.splits_auto(1, 7, w.Sq, w.Sk)
-    ws = torch.empty(max(1, qfa.split_workspace_bytes(1, 7, w.Sq, w.D, ns)), dtype=torch.uint8, device=dev)
-    line = {"config": "band_shard_h7_split_k", "shape": f"B1 H7 Sq{w.Sq} Sk{w.Sk} D{w.D} bf16, fp32 bias, LSE on",
-            "auto_splits": ns}
-    fl = 4.0 * 7 * w.Sq * w.Sk * w.D
-    for n in sorted({1, 2, ns, 8}):
-        wsn = ws if n == ns else None
-        t = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=bias, out=out, lse=lse, splits=n, workspace=wsn), 10)
-        line[f"splits{n}_ms"] = round(t, 4)
-        line[f"splits{n}_frac_blend"] = round(fl / (t * 1e-3) / 1e12 / PEAK_BLEND, 4)
-    line["device"] = info
-    print(json.dumps(line), flush=True)
-    del q, k, v, bias, qk, out, lse, ws
-    torch.cuda.empty_cache()
+    if sel("sparse"):
+        w = W.WORKLOADS["sparse"]
+        T = w.Sk // 64
+        mask_np = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
+        vbs_np = W.sparse_vbs(T, w.extras["last_valid"])
+        q_np, k_np, v_np = W.make_qkv(w)
+        for x in (q_np, k_np, v_np):
+            W.zero_pads(x, vbs_np)
+        q, k, v = up(q_np), up(k_np), up(v_np)
+        del q_np, k_np, v_np
+        mask, vbs, vsc = up(mask_np.astype(np.uint8)), up(vbs_np), up(W.v_scale(w))
+        ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
+        qk = qfa.quantize_qk(q, k, vbs=vbs, workspace=ws)
+        idx, cnt = qfa.blockmask_to_index(mask)
+        out = torch.empty_like(q)
+        t_m = _time_ms(lambda: qfa.blockmask_to_index(mask), 20)
+        t_q = _time_ms(lambda: qfa.quantize_qk(q, k, vbs=vbs, workspace=ws), 10)
+        t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, index=idx, count=cnt, vbs=vbs, v_scale=vsc, out=out), 10)
+        pairs = int(mask_np.sum())
+        fl = 4.0 * w.D * 64 * 64 * pairs
+        mb = mask_np.size + pairs * 4 + w.B * w.H * T * 4   # mask bytes read; entries + counts written
+        qb = qbytes(w.B, w.H, w.Sq, w.Sk, w.D, 2)
+        print(json.dumps({
+            "config": "sparse", "shape": f"B{w.B} H{w.H} S{w.Sq} D{w.D} {w.dtype}, tile-64 mask prefix 8 + band 48",
+            "tile_pairs": pairs, "map_to_index_ms": round(t_m, 4), "map_to_index_GBps": round(mb / (t_m * 1e-3) / 1e9, 1),
+            "quantize_ms": round(t_q, 4), "quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
+            "attn_ms": round(t_a, 4), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
+            "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
+            "end_to_end_ms": round(t_m + t_q + t_a, 4), "device": info}), flush=True)
+        del q, k, v, qk, out, idx, cnt, mask, ws
+        torch.cuda.empty_cache()
 
-    # the banded workload with the pages' bool [1,1,1,K] keep mask (raised-cosine weight > 1e-3)
-    w = W.WORKLOADS["band"]
-    q_np, k_np, v_np = W.make_qkv(w)
-    q, k, v = up(q_np), up(k_np), up(v_np)
-    del q_np, k_np, v_np
-    weights = np.exp(W.band_bias(w.Sk, core=w.extras["core"], skirt=w.extras["skirt"]))
-    keep = torch.from_numpy((weights > 1e-3).reshape(1, 1, 1, -1)).to(dev)
-    ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
-    qk = qfa.quantize_qk(q, k, workspace=ws)
-    out = torch.empty_like(q)
-    t_u = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, out=out), 10)
-    t_k = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, bias=keep, out=out), 10)
-    print(json.dumps({
-        "config": "band_keep_mask", "shape": f"B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} D{w.D} {w.dtype}",
-        "kept_keys": int(keep.sum().item()), "unmasked_ms": round(t_u, 4), "keep_mask_ms": round(t_k, 4),
-        "keep_over_unmasked": round(t_k / t_u, 3), "device": info}), flush=True)
-    del q, k, v, qk, out, keep, ws
-    torch.cuda.empty_cache()
+    if sel("gemm_reference"):
+        # matrix-core reference through torch (hipBLASLt / rocBLAS): 8192^3 GEMMs
+        n = 8192
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        t_bf = _time_ms(lambda: torch.matmul(a, b), 10)
+        gemm = {"bf16_tflops": round(2.0 * n ** 3 / (t_bf * 1e-3) / 1e12, 1)}
+        try:
+            a8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+            b8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+            t_i8 = _time_ms(lambda: torch._int_mm(a8, b8), 10)
+            gemm["int8_tops"] = round(2.0 * n ** 3 / (t_i8 * 1e-3) / 1e12, 1)
+        except (RuntimeError, AttributeError) as e:
+            gemm["int8_tops"] = None
+            gemm["int8_note"] = str(e).splitlines()[0][:120]
+        print(json.dumps({"config": "gemm_reference", "m=n=k": n, **gemm,
+                          "published_dense_peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "int8_tops": PEAK_I8_TOPS},
+                          "device": info}), flush=True)
 
-    w = W.WORKLOADS["sparse"]
-    T = w.Sk // 64
-    mask_np = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
-    vbs_np = W.sparse_vbs(T, w.extras["last_valid"])
-    q_np, k_np, v_np = W.make_qkv(w)
-    for x in (q_np, k_np, v_np):
-        W.zero_pads(x, vbs_np)
-    q, k, v = up(q_np), up(k_np), up(v_np)
-    del q_np, k_np, v_np
-    mask, vbs, vsc = up(mask_np.astype(np.uint8)), up(vbs_np), up(W.v_scale(w))
-    ws = torch.empty(qfa.quantize_workspace_bytes(w.B, w.H, w.Sk, w.D), dtype=torch.uint8, device=dev)
-    qk = qfa.quantize_qk(q, k, vbs=vbs, workspace=ws)
-    idx, cnt = qfa.blockmask_to_index(mask)
-    out = torch.empty_like(q)
-    t_m = _time_ms(lambda: qfa.blockmask_to_index(mask), 20)
-    t_q = _time_ms(lambda: qfa.quantize_qk(q, k, vbs=vbs, workspace=ws), 10)
-    t_a = _time_ms(lambda: qfa.attn_fwd(qk, v, w.sm_scale, index=idx, count=cnt, vbs=vbs, v_scale=vsc, out=out), 10)
-    pairs = int(mask_np.sum())
-    fl = 4.0 * w.D * 64 * 64 * pairs
-    mb = mask_np.size + pairs * 4 + w.B * w.H * T * 4   # mask bytes read; entries + counts written
-    qb = qbytes(w.B, w.H, w.Sq, w.Sk, w.D, 2)
-    print(json.dumps({
-        "config": "sparse", "shape": f"B{w.B} H{w.H} S{w.Sq} D{w.D} {w.dtype}, tile-64 mask prefix 8 + band 48",
-        "tile_pairs": pairs, "map_to_index_ms": round(t_m, 4), "map_to_index_GBps": round(mb / (t_m * 1e-3) / 1e9, 1),
-        "quantize_ms": round(t_q, 4), "quantize_GBps": round(qb / (t_q * 1e-3) / 1e9, 1),
-        "attn_ms": round(t_a, 4), "attn_tflops": round(fl / (t_a * 1e-3) / 1e12, 1),
-        "attn_frac_blend": round(fl / (t_a * 1e-3) / 1e12 / PEAK_BLEND, 4),
-        "end_to_end_ms": round(t_m + t_q + t_a, 4), "device": info}), flush=True)
-    del q, k, v, qk, out, idx, cnt, mask, ws
-    torch.cuda.empty_cache()
+    return 0
 
-    # matrix-core reference through torch (hipBLASLt / rocBLAS): 8192^3 GEMMs
-    n = 8192
-    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
-    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
-    t_bf = _time_ms(lambda: torch.matmul(a, b), 10)
-    gemm = {"bf16_tflops": round(2.0 * n ** 3 / (t_bf * 1e-3) / 1e12, 1)}
-    try:
-        a8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
-        b8 = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
-        t_i8 = _time_ms(lambda: torch._int_mm(a8, b8), 10)
-        gemm["int8_tops"] = round(2.0 * n ** 3 / (t_i8 * 1e-3) / 1e12, 1)
-    except (RuntimeError, AttributeError) as e:
-        gemm["int8_tops"] = None
-        gemm["int8_note"] = str(e).splitlines()[0][:120]
-    print(json.dumps({"config": "gemm_reference", "m=n=k": n, **gemm,
-                      "published_dense_peaks": {"bf16_tflops": PEAK_BF16_TFLOPS, "int8_tops": PEAK_I8_TOPS},
-                      "device": info}), flush=True)
+
+def _time_rotated(dev, fns, rounds: int):
+    """Median milliseconds per call of fns[0], fns[1], ... cycled `rounds` times (HIP events on
+    the current stream around each call). A run of 1 GiB fills is queued first: it flushes the
+    256 MB MALL and keeps the GPU busy while the host enqueues the calls, so the host's call
+    overhead stays out of the events."""
+    import torch
+
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    busy = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(max(8, len(fns) * rounds // 2)):
+        busy.fill_(1.0)
+    evs = []
+    for _ in range(rounds):
+        for f in fns:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del busy
+    return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+BW_ROWS = ("copy", "quantize_c2", "quantize_c3", "quantize_c4", "quantize_c5", "merge_c4", "map_to_index_c5")
+
+
+def bandwidth(dev, only=None) -> int:
+    """One JSON line: the bandwidth-bound calls (quantize on the dense 4k, d64, banded and
+    block-sparse shapes; the LSE merge of the banded split; the tile-mask map-to-index of the
+    block-sparse shape) timed over >= 3 rotated input/output sets totalling more than the 256 MB
+    MALL, so every call streams from HBM. Quantize bytes follow the algorithmic model (read Q and
+    K once; write Q8, K8, qs, ks, the K mean and the centring term); the kernel's second read of
+    K (mean, then codes) is reported as a separate figure. A plain device copy, rotated the same
+    way, gives the rate the machine's HBM sustains for a read+write stream. Inputs are N(0,1) drawn on
+    the GPU (the dense 4k K with its per-channel offset, the block-sparse pad rows zero): the
+    calls' cost does not depend on the values."""
+    import numpy as np
+    import torch
+
+    import quantized_flash_attention_amd as qfa
+    import workloads as W
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(101)
+    rows = []
+    want = set(only.split(",")) if only else set(BW_ROWS)
+    bad = want - set(BW_ROWS)
+    if bad:
+        print(f"bench.py: unknown --only rows {sorted(bad)}; known: {', '.join(BW_ROWS)}", file=sys.stderr)
+        return 2
+
+    def nsets(set_bytes):
+        return max(3, -(-(300 << 20) // set_bytes))
+
+    def rate(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    if "copy" in want:
+        n = 256 << 20
+        sets = [(torch.empty(n, dtype=torch.uint8, device=dev), torch.empty(n, dtype=torch.uint8, device=dev))
+                for _ in range(3)]
+        ms = _time_rotated(dev, [lambda s=s: s[1].copy_(s[0]) for s in sets], 6)
+        rows.append({"row": "copy", "what": "device copy of 256 MiB (read + write)", "sets": 3,
+                     "bytes": 2 * n, "ms": round(ms, 4), "GBps": rate(2 * n, ms),
+                     "frac_hbm": round(2 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        del sets
+
+    for tag, name in (("c2", "dense4k"), ("c3", "d64"), ("c4", "band"), ("c5", "sparse")):
+        if f"quantize_{tag}" not in want:
+            continue
+        w = W.WORKLOADS[name]
+        B, H, Sq, Sk, D = w.B, w.H, w.Sq, w.Sk, w.D
+        Hkv = w.extras.get("hkv", H)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        in_bytes = (B * H * Sq + B * Hkv * Sk) * D * 2
+        model = in_bytes + (B * H * Sq + B * Hkv * Sk) * (D + 4) + B * Hkv * D * 4 + B * H * Sq * 4
+        second_k = B * Hkv * Sk * D * 2
+        n = nsets(model)
+        vbs = None
+        if name == "sparse":
+            vbs = torch.from_numpy(W.sparse_vbs(Sk // 64, w.extras["last_valid"])).to(dev)
+        sets = []
+        for _ in range(n):
+            q = torch.randn((B, H, Sq, D), generator=gen, device=dev, dtype=torch.float32).to(dt)
+            k = torch.randn((B, Hkv, Sk, D), generator=gen, device=dev, dtype=torch.float32)
+            if "k_offset_std" in w.extras:
+                k += torch.randn((D,), generator=gen, device=dev) * w.extras["k_offset_std"]
+            k = k.to(dt)
+            if vbs is not None:
+                last = Sk - 64 + w.extras["last_valid"]
+                q[:, :, last:] = 0
+                k[:, :, last:] = 0
+            out = dict(q8=torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev),
+                       qs=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
+                       k8=torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev),
+                       ks=torch.empty((B, Hkv, Sk), dtype=torch.float32, device=dev),
+                       kmean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev),
+                       qmu=torch.empty((B, H, Sq), dtype=torch.float32, device=dev))
+            ws = torch.empty(qfa.quantize_workspace_bytes(B, Hkv, Sk, D), dtype=torch.uint8, device=dev)
+            sets.append((q, k, out, ws))
+        fns = [lambda s=s: qfa.quantize_qk(s[0], s[1], vbs=vbs, workspace=s[3], out=s[2]) for s in sets]
+        ms = _time_rotated(dev, fns, max(2, 12 // n))
+        rows.append({"row": f"quantize_{tag}", "shape": f"B{B} H{H} Sq{Sq} Sk{Sk} D{D} {w.dtype}", "sets": n,
+                     "model_MB": round(model / 1e6, 1), "second_k_read_MB": round(second_k / 1e6, 1),
+                     "ms": round(ms, 4), "GBps_model": rate(model, ms),
+                     "frac_hbm_model": round(model / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                     "GBps_with_second_k_read": rate(model + second_k, ms)})
+        del sets, fns
+        torch.cuda.empty_cache()
+
+    if "merge_c4" in want:
+        w = W.WORKLOADS["band"]
+        B, H, S, D = w.B, w.H, w.Sq, w.D
+        nbytes = B * H * S * (2 * D * 4 + 2 * 4 + D * 2 + 4)
+        n = nsets(nbytes)
+        sets = []
+        for _ in range(n):
+            oa = torch.randn((B, H, S, D), generator=gen, device=dev)
+            ob = torch.randn((B, H, S, D), generator=gen, device=dev)
+            la = torch.randn((B, H, S), generator=gen, device=dev)
+            lb = torch.randn((B, H, S), generator=gen, device=dev)
+            sets.append((oa, la, ob, lb, torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev),
+                         torch.empty((B, H, S), dtype=torch.float32, device=dev)))
+        fns = [lambda s=s: qfa.lse_merge(s[0], s[1], s[2], s[3], out=s[4], lse_out=s[5]) for s in sets]
+        ms = _time_rotated(dev, fns, 4)
+        rows.append({"row": "merge_c4", "shape": f"B{B} H{H} S{S} D{D}: two fp32 partials + LSE -> bf16 + LSE",
+                     "sets": n, "MB": round(nbytes / 1e6, 1), "ms": round(ms, 4), "GBps": rate(nbytes, ms),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        del sets, fns
+        torch.cuda.empty_cache()
+
+    if "map_to_index_c5" in want:
+        w = W.WORKLOADS["sparse"]
+        T = w.Sk // 64
+        mask_np = W.sparse_mask(T, w.H, w.extras["prefix"], w.extras["band"])
+        pairs = int(mask_np.sum())
+        nbytes = mask_np.size + pairs * 4 + w.B * w.H * T * 4   # mask read; entries + counts written
+        n = nsets(nbytes)
+        m0 = torch.from_numpy(mask_np.astype(np.uint8)).to(dev)
+        masks = [m0.clone() for _ in range(n)]
+        del m0
+        fns = [lambda m=m: qfa.blockmask_to_index(m) for m in masks]
+        ms = _time_rotated(dev, fns, 4)
+        rows.append({"row": "map_to_index_c5", "shape": f"mask [1,{w.H},{T},{T}] uint8, {pairs} kept tile pairs",
+                     "sets": n, "MB": round(nbytes / 1e6, 1), "ms": round(ms, 4), "GBps": rate(nbytes, ms),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        del masks, fns
+        torch.cuda.empty_cache()
+
+    print(json.dumps({"config": "bandwidth", "what": "bandwidth-bound calls over rotated sets (> 256 MB in total)",
+                      "rows": rows, "device": device_info(dev)}), flush=True)
     return 0
 
 

@@ -66,14 +66,7 @@ def quantize_workspace_bytes(B: int, H: int, Sk: int, D: int) -> int:
     return n.value
 
 
-def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = None, center_k: bool = True,
-                workspace: torch.Tensor | None = None) -> dict:
-    """Per-token symmetric int8 Q/K (+ K mean, centring term) on the GPU.
-
-    K may hold fewer heads than Q (grouped-query attention: query head h shares K/V head
-    h // (H // Hkv)); the K outputs then have Hkv heads.
-    Returns dict(q8, qs, k8, ks, kmean, qmu); kmean/qmu are None when center_k is False.
-    """
+def _quant_inputs(q, k, vbs):
     _no_grad(q, k)
     B, H, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
@@ -81,22 +74,56 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = Non
         raise ValueError("q and k must agree in B, D and dtype")
     dq, *qst = _view(q, "q")
     _, *kst = _view(k, "k")
+    return (B, H, Hkv, Sq, Sk, D), dq, qst, kst, _cont(vbs, "vbs", torch.int32)
+
+
+def _quant_outputs(dims, center_k: bool, out: dict | None, dev) -> dict:
+    """The output tensors of a quantize call: those of ``out`` (checked: shape, dtype, contiguity,
+    device; kmean and qmu required exactly when K is centred), else new ones."""
+    B, H, Hkv, Sq, Sk, D = dims
+    want = dict(q8=((B, H, Sq, D), torch.int8), qs=((B, H, Sq), torch.float32),
+                k8=((B, Hkv, Sk, D), torch.int8), ks=((B, Hkv, Sk), torch.float32),
+                kmean=((B, Hkv, D), torch.float32), qmu=((B, H, Sq), torch.float32))
+    if not center_k:
+        want.pop("kmean"), want.pop("qmu")
+    if out is None:
+        out = {n: torch.empty(shape, dtype=dt, device=dev) for n, (shape, dt) in want.items()}
+        out.setdefault("kmean", None), out.setdefault("qmu", None)
+        return out
+    for n, (shape, dt) in want.items():
+        t = out.get(n)
+        if t is None:
+            raise ValueError(f"out[{n!r}] is required")
+        _shape(t, n, shape)
+        _cont(t, n, dt)
+        if t.device != dev:
+            raise ValueError(f"out[{n!r}] is on {t.device}, the inputs on {dev}")
+    if not center_k and (out.get("kmean") is not None or out.get("qmu") is not None):
+        raise ValueError("kmean and qmu are outputs of a centred call only (center_k=True)")
+    return dict(out, kmean=out.get("kmean"), qmu=out.get("qmu"))
+
+
+def quantize_qk(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = None, center_k: bool = True,
+                workspace: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """Per-token symmetric int8 Q/K (+ K mean, centring term) on the GPU.
+
+    K may hold fewer heads than Q (grouped-query attention: query head h shares K/V head
+    h // (H // Hkv)); the K outputs then have Hkv heads.
+    Returns dict(q8, qs, k8, ks, kmean, qmu); kmean/qmu are None when center_k is False. With
+    ``out`` (a dict of those keys) the results land in its tensors.
+    """
+    dims, dq, qst, kst, vbs = _quant_inputs(q, k, vbs)
+    B, H, Hkv, Sq, Sk, D = dims
     dev = q.device
-    vbs = _cont(vbs, "vbs", torch.int32)
-    q8 = torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev)
-    k8 = torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev)
-    qs = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    ks = torch.empty((B, Hkv, Sk), dtype=torch.float32, device=dev)
-    kmean = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if center_k else None
-    qmu = torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if center_k else None
+    out = _quant_outputs(dims, center_k, out, dev)
     nbytes = quantize_workspace_bytes(B, Hkv, Sk, D) if center_k else 0
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _lib.check(_lib.lib().qfa_quantize_qk(
         B, H, Hkv, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
-        _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(kmean), _ptr(qmu),
+        _ptr(out["q8"]), _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out["kmean"]), _ptr(out["qmu"]),
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev)))
-    return dict(q8=q8, qs=qs, k8=k8, ks=ks, kmean=kmean, qmu=qmu)
+    return out
 
 
 def quantize_qk_noalloc(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | None = None, center_k: bool = True,
@@ -104,31 +131,14 @@ def quantize_qk_noalloc(q: torch.Tensor, k: torch.Tensor, vbs: torch.Tensor | No
     """:func:`quantize_qk` through qfa_quantize_qk_noalloc: the library allocates nothing (its K-mean
     partials live in static device memory); the outputs are the tensors of ``out`` (keys q8, qs, k8,
     ks, kmean, qmu as :func:`quantize_qk` returns them), allocated here only when it is None."""
-    _no_grad(q, k)
-    B, H, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
-    if k.shape[0] != B or k.shape[3] != D or k.dtype != q.dtype:
-        raise ValueError("q and k must agree in B, D and dtype")
-    dq, *qst = _view(q, "q")
-    _, *kst = _view(k, "k")
+    dims, dq, qst, kst, vbs = _quant_inputs(q, k, vbs)
+    B, H, Hkv, Sq, Sk, D = dims
     dev = q.device
-    vbs = _cont(vbs, "vbs", torch.int32)
-    if out is None:
-        out = dict(q8=torch.empty((B, H, Sq, D), dtype=torch.int8, device=dev),
-                   qs=torch.empty((B, H, Sq), dtype=torch.float32, device=dev),
-                   k8=torch.empty((B, Hkv, Sk, D), dtype=torch.int8, device=dev),
-                   ks=torch.empty((B, Hkv, Sk), dtype=torch.float32, device=dev),
-                   kmean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if center_k else None,
-                   qmu=torch.empty((B, H, Sq), dtype=torch.float32, device=dev) if center_k else None)
-    _shape(out["q8"], "q8", (B, H, Sq, D)), _shape(out["k8"], "k8", (B, Hkv, Sk, D))
-    _shape(out["qs"], "qs", (B, H, Sq)), _shape(out["ks"], "ks", (B, Hkv, Sk))
-    _cont(out["q8"], "q8", torch.int8), _cont(out["k8"], "k8", torch.int8)
-    _cont(out["qs"], "qs", torch.float32), _cont(out["ks"], "ks", torch.float32)
-    _cont(out.get("kmean"), "kmean", torch.float32), _cont(out.get("qmu"), "qmu", torch.float32)
+    out = _quant_outputs(dims, center_k, out, dev)
     _lib.check(_lib.lib().qfa_quantize_qk_noalloc(
         B, H, Hkv, Sq, Sk, D, dq, _ptr(q), *qst, _ptr(k), *kst, _ptr(vbs), int(center_k),
-        _ptr(out["q8"]), _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out.get("kmean")),
-        _ptr(out.get("qmu")), _stream(dev)))
+        _ptr(out["q8"]), _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out["kmean"]),
+        _ptr(out["qmu"]), _stream(dev)))
     return out
 
 

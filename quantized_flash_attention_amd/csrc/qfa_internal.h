@@ -10,15 +10,18 @@ namespace qfa {
 enum DType : int { BF16 = 1, FP16 = 2, FP32 = 3, BOOL = 4 };
 
 // Quantize step: K mean, then int8 codes of every Q and K row.
-//  - The K mean is summed in double-double partials over at most
-//    kMeanMaxChunks row chunks per (b, K/V head), at most kMeanSlots partials
-//    in all (fewer chunks per head when B*Hkv is large); a second small
-//    launch combines each head's partials into the mean. (Combining them in
-//    the last block of each head instead needs a device-scope fence in every
+//  - The K mean is summed in double-double partials over row chunks of at
+//    least kMeanMinChunkRows rows per (b, K/V head), at most kMeanMaxChunks
+//    chunks per head and kMeanSlots in all (fewer chunks per head when B*Hkv
+//    is large). Smaller chunks measured slower on short heads (more partials
+//    to combine, blocks too short to hide their start-up); the chunk cap
+//    lets long heads spread over the whole chip. A second small launch
+//    combines each head's partials into the mean. (Combining them in the
+//    last block of each head instead needs a device-scope fence in every
 //    block, an L2-wide write-back and invalidate that serialise per XCD: it
 //    measured 8x slower than the whole partial pass.)
 //  - One launch then quantizes all K rows (centred) and all Q rows.
-constexpr int kMeanMaxChunks = 64;
+constexpr int kMeanMaxChunks = 256;
 constexpr int64_t kMeanSlots = 4096;
 constexpr int64_t kMeanMinChunkRows = 256;
 

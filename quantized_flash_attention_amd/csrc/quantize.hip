@@ -9,8 +9,8 @@
 //
 // Three launches, the two big ones HBM-bound streaming passes with 16-byte
 // loads and one row of D channels spread over D/8 lanes:
-//   kmean_partial_kernel   exact column sums of K over at most 64 row chunks
-//                          per (b, K/V head)
+//   kmean_partial_kernel   exact column sums of K over row chunks of each
+//                          (b, K/V head)
 //   kmean_finalize_kernel  each head's chunk sums combined (exactly, so in any
 //                          order) into the mean: a few KB per head
 //   quantize_kernel        every K row (centred), then every Q row (and q.mu):

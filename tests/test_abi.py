@@ -49,11 +49,12 @@ def test_probe_library_exports_its_header():
 
 
 def test_workspace_size():
-    """K-mean partials: up to 64 chunks of at least 256 rows per (b, K/V head), at most 4096 in all,
-    16 bytes per channel."""
+    """K-mean partials: chunks of at least 256 rows, up to 256 per (b, K/V head) and 4096 in all, 16
+    bytes per channel."""
     n = qfa.quantize_workspace_bytes(1, 56, 33600, 128)
-    assert n == 56 * 64 * 128 * 16                    # 132 chunks of 256 rows capped at 64
+    assert n == 56 * 73 * 128 * 16                    # 132 chunks of 256 rows, 4096 slots in all
     assert qfa.quantize_workspace_bytes(1, 20, 9216, 64) == 20 * 36 * 64 * 16
+    assert qfa.quantize_workspace_bytes(1, 2, 1 << 20, 128) == 2 * 256 * 128 * 16   # at most 256 per head
     assert qfa.quantize_workspace_bytes(8, 128, 4096, 128) == 1024 * 4 * 128 * 16   # 4096 slots in all
     assert qfa.quantize_workspace_bytes(1, 5000, 300, 64) == 5000 * 64 * 16          # one chunk each
     assert qfa.quantize_workspace_bytes(1, 3, 100, 64) == 3 * 64 * 16
@@ -253,3 +254,29 @@ def test_python_binding_refuses_grad_and_bad_bias():
     v = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="query dim"):
         qfa.attn_fwd(qk, v, bias=torch.zeros(1, 1, 7, 64))
+
+
+def test_python_binding_checks_quantize_outputs():
+    # caller-provided outputs are checked before any call into the library
+    import torch
+    q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 96, 128, dtype=torch.bfloat16)
+
+    def outs(**over):
+        o = dict(q8=torch.zeros(1, 2, 64, 128, dtype=torch.int8), qs=torch.zeros(1, 2, 64),
+                 k8=torch.zeros(1, 2, 96, 128, dtype=torch.int8), ks=torch.zeros(1, 2, 96),
+                 kmean=torch.zeros(1, 2, 128), qmu=torch.zeros(1, 2, 64))
+        o.update(over)
+        return o
+
+    for fn in (qfa.quantize_qk, qfa.quantize_qk_noalloc):
+        with pytest.raises(ValueError, match="kmean shape"):
+            fn(q, k, out=outs(kmean=torch.zeros(1, 2, 64)))
+        with pytest.raises(ValueError, match="qmu shape"):
+            fn(q, k, out=outs(qmu=torch.zeros(1, 2, 63)))
+        with pytest.raises(ValueError, match="required"):
+            fn(q, k, out=outs(qmu=None))
+        with pytest.raises(ValueError, match="k8 must be a contiguous"):
+            fn(q, k, out=outs(k8=torch.zeros(1, 2, 96, 128, dtype=torch.uint8)))
+        with pytest.raises(ValueError, match="centred call only"):
+            fn(q, k, center_k=False, out=outs())

@@ -54,7 +54,7 @@ def _same(a, b, what):
 
 CALLS = [
     # (workload, B, H, Hkv, Sq, Sk, vbs, centre): each call smaller than the one before
-    ("band", 1, 8, 8, 700, 20000, None, True),      # 64 chunks of 313 rows per head
+    ("band", 1, 8, 8, 700, 20000, None, True),      # 79 chunks of 254 rows per head
     ("dense4k", 2, 4, 2, 1000, 3000, None, True),   # grouped-query, 12 chunks per head
     ("d64", 1, 3, 3, 300, 517, None, True),         # fp16, D = 64
     ("sparse", 1, 2, 2, 320, 320, "vbs", True),     # validity vector: pads out of the mean
