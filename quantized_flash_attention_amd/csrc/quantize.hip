@@ -65,13 +65,15 @@ __device__ __forceinline__ bool is_pad(const int32_t* vbs, int64_t j) {
 // partial slot.
 //
 // Each lane sums its values of a channel in plain fp64, which is exact when
-// every partial sum is representable: fp16 values are multiples of 2^-24 below
-// 2^16, so any sum of fewer than 2^13 of them is; a lane of bf16 values tracks
-// its largest and smallest nonzero magnitude, and the sum is exact when
-// (exponent span) + 8 significand bits + log2(values summed) <= 53, as every
-// value is then a multiple of the smallest one's ulp. A lane whose bf16 values
-// span more (tiny values beside large ones, subnormals) sums its rows again in
-// double-double. The slots' sums are combined in double-double.
+// every partial sum is representable. The lane tracks its largest and smallest
+// nonzero magnitude; every value is a multiple of 2^(emin - (P - 1)) for the
+// smallest one's exponent emin and the input's P significand bits (8 for
+// bf16, 11 for fp16, whose subnormals are multiples of 2^-24 and so qualify
+// too), and every partial sum stays below 2^(emax + 1) times the count, so the
+// sum is exact when (emax - emin) + P + log2(values summed) <= 53. A lane whose
+// values span more (tiny values beside large ones, bf16 subnormals, a NaN or
+// inf) sums its rows again in double-double. The slots' sums are combined in
+// double-double.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nchunks, int64_t chunk_rows) {
   constexpr int G = D / 8;          // lanes per row
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nch
   double fsum[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) fsum[i] = 0.0;
-  // bf16: largest magnitude, and smallest nonzero magnitude minus one (as
-  // unsigned bits, so a zero wraps to the top and never counts)
+  // largest magnitude, and smallest nonzero magnitude minus one (fp32 bits,
+  // unsigned, so a zero wraps to the top and never counts)
   uint32_t amax = 0u, amin_m1 = 0xffffffffu;
   int64_t nvals = 0;   // values this lane adds per channel
   for (int64_t j = r0 + rs; j < r1; j += RP * U) {
@@ -110,23 +112,22 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(QuantArgs a, int nch
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         fsum[i] += (double)f[i];
-        if (DT == BF16) {
-          const uint32_t m = __float_as_uint(f[i]) & 0x7fffffffu;
-          amax = max(amax, m);
-          amin_m1 = min(amin_m1, m - 1u);
-        }
+        const uint32_t m = __float_as_uint(f[i]) & 0x7fffffffu;
+        amax = max(amax, m);
+        amin_m1 = min(amin_m1, m - 1u);
       }
     }
   }
   bool exact = true;
-  if (DT == BF16 && amax != 0u) {
-    // exponents of the extreme magnitudes (a subnormal counts as 2^-149,
-    // which always fails the test below)
+  if (amax != 0u) {
+    constexpr int P = DT == BF16 ? 8 : 11;   // significand bits of the input type
+    // exponents of the extreme magnitudes (an fp32 subnormal, i.e. a bf16
+    // one, counts as 2^-149, which always fails the test below)
     const int emax = (int)(amax >> 23) - 127;
     const uint32_t amin = amin_m1 + 1u;
     const int emin = (amin >> 23) == 0u ? -149 : (int)(amin >> 23) - 127;
     const int lgn = 64 - __clzll((unsigned long long)max(nvals, (int64_t)1));   // > log2(nvals)
-    exact = emax - emin + 8 + lgn <= 53;
+    exact = emax - emin + P + lgn <= 53;
   }
   DD acc[8];
   if (exact) {

@@ -1186,10 +1186,10 @@ def test_debug_log_names_the_instance():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_kmean_wide_exponent_spans(dtype):
-    """K-mean exactness where a plain fp64 sum would round: channels mixing values near 2^30 (bf16) or
-    6e4 (fp16) with values near 2^-60 (bf16) or subnormal fp16, exact zeros and a bf16 subnormal (12
-    chunks of 250 rows per head, lanes holding both extremes); the kernel's double-double path for such lanes must reproduce the
-    oracle's exact mean bit for bit."""
+    """K-mean exactness where the kernel's plain fp64 sum is not certified exact: channels mixing values
+    near 2^30 (bf16) or 6e4 (fp16) with values near 2^-60 (bf16) or subnormal fp16, exact zeros and a
+    bf16 subnormal (12 chunks of 250 rows per head, lanes holding both extremes); the kernel's
+    double-double path for such lanes must reproduce the oracle's exact mean bit for bit."""
     w = W.WORKLOADS["dense4k"]
     q, k, _ = W.make_qkv(w, H=3, Sq=64, Sk=3000)
     kf = W.to_f32(k)
