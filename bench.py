@@ -297,6 +297,24 @@ def main() -> int:
     except (OSError, RuntimeError) as e:
         out["roofline"]["measured_mfma_ceiling"] = {"error": str(e)[:200]}
 
+    # the step's bandwidth-bound calls again, over rotated input sets that do not fit the MALL
+    try:
+        del q, k, v, o_un, o_bias, o_core, o_skirt, o_split, qk, ws
+        torch.cuda.empty_cache()
+        bw = {r["row"]: r for r in bandwidth_rows(dev, ["copy", "quantize_c4", "merge_c4"])}
+        out["bandwidth_rotated"] = {
+            "sets": "3 per call, > 256 MB in total",
+            "copy_GBps": bw["copy"]["GBps"],
+            "quantize_ms": bw["quantize_c4"]["ms"], "quantize_model_MB": bw["quantize_c4"]["model_MB"],
+            "quantize_GBps_model": bw["quantize_c4"]["GBps_model"],
+            "quantize_frac_hbm_model": bw["quantize_c4"]["frac_hbm_model"],
+            "quantize_second_k_read_MB": bw["quantize_c4"]["second_k_read_MB"],
+            "quantize_GBps_with_second_k_read": bw["quantize_c4"]["GBps_with_second_k_read"],
+            "merge_ms": bw["merge_c4"]["ms"], "merge_GBps": bw["merge_c4"]["GBps"],
+            "merge_frac_hbm": bw["merge_c4"]["frac_hbm"]}
+    except RuntimeError as e:
+        out["bandwidth_rotated"] = {"error": str(e)[:200]}
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -799,7 +817,19 @@ BW_ROWS = ("copy", "quantize_c2", "quantize_c3", "quantize_c4", "quantize_c5", "
 
 
 def bandwidth(dev, only=None) -> int:
-    """One JSON line: the bandwidth-bound calls (quantize on the dense 4k, d64, banded and
+    """One JSON line of bandwidth_rows (below)."""
+    want = only.split(",") if only else list(BW_ROWS)
+    bad = set(want) - set(BW_ROWS)
+    if bad:
+        print(f"bench.py: unknown --only rows {sorted(bad)}; known: {', '.join(BW_ROWS)}", file=sys.stderr)
+        return 2
+    print(json.dumps({"config": "bandwidth", "what": "bandwidth-bound calls over rotated sets (> 256 MB in total)",
+                      "rows": bandwidth_rows(dev, want), "device": device_info(dev)}), flush=True)
+    return 0
+
+
+def bandwidth_rows(dev, want) -> list:
+    """The bandwidth-bound calls (quantize on the dense 4k, d64, banded and
     block-sparse shapes; the LSE merge of the banded split; the tile-mask map-to-index of the
     block-sparse shape) timed over >= 3 rotated input/output sets totalling more than the 256 MB
     MALL, so every call streams from HBM. Quantize bytes follow the algorithmic model (read Q and
@@ -817,11 +847,7 @@ def bandwidth(dev, only=None) -> int:
     gen = torch.Generator(device=dev)
     gen.manual_seed(101)
     rows = []
-    want = set(only.split(",")) if only else set(BW_ROWS)
-    bad = want - set(BW_ROWS)
-    if bad:
-        print(f"bench.py: unknown --only rows {sorted(bad)}; known: {', '.join(BW_ROWS)}", file=sys.stderr)
-        return 2
+    want = set(want)
 
     def nsets(set_bytes):
         return max(3, -(-(300 << 20) // set_bytes))
@@ -921,9 +947,7 @@ def bandwidth(dev, only=None) -> int:
         del masks, fns
         torch.cuda.empty_cache()
 
-    print(json.dumps({"config": "bandwidth", "what": "bandwidth-bound calls over rotated sets (> 256 MB in total)",
-                      "rows": rows, "device": device_info(dev)}), flush=True)
-    return 0
+    return rows
 
 
 def cpu_model() -> str:
