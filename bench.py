@@ -75,7 +75,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--variant-iters", type=int, default=20, help="iterations of each per-call timing loop")
+    ap.add_argument("--variant-iters", type=int, default=100, help="timed iterations of each per-call loop")
+    ap.add_argument("--variant-warmup", type=int, default=50, help="warm-up iterations of each per-call loop")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows per head the oracle computes")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads the oracle computes (about 13 s on 16 cores)")
@@ -193,18 +194,38 @@ def main() -> int:
     med = {n: statistics.median(x) for n, x in per.items()}
     mean = {n: statistics.fmean(x) for n, x in per.items()}
 
-    # bf16-bias single call: its own loop (same kernel instance as the fp32 bias call)
+    # each variant in a loop of its own: warm-ups, then timed calls (median and min); the bf16-bias
+    # call runs only here (same kernel instance as the fp32 bias call)
     qk = step()
     torch.cuda.synchronize()
-    bf = []
-    for _ in range(args.variant_iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        qfa.attn_fwd(qk, v, sm, bias=bias16, out=o_bias)
-        e1.record(stream)
-        bf.append((e0, e1))
-    torch.cuda.synchronize()
-    med["bias_bf16"] = statistics.median(a.elapsed_time(b) for a, b in bf)
+
+    def loop(fn):
+        for _ in range(args.variant_warmup):
+            fn()
+        evs = []
+        for _ in range(args.variant_iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        return {"median_ms": round(statistics.median(ts), 4), "min_ms": round(min(ts), 4)}
+
+    def split_call():
+        qfa.attn_fwd(qk, v, sm, segments=[core], out=o_core, lse=l_core)
+        qfa.attn_fwd(qk, v, sm, bias=bias32, segments=skirts, out=o_skirt, lse=l_skirt)
+        qfa.lse_merge(o_core, l_core, o_skirt, l_skirt, out=o_split, lse_out=l_split)
+
+    variants = {
+        "unmasked": loop(lambda: qfa.attn_fwd(qk, v, sm, out=o_un)),
+        "bias_fp32": loop(lambda: qfa.attn_fwd(qk, v, sm, bias=bias32, out=o_bias)),
+        "bias_bf16": loop(lambda: qfa.attn_fwd(qk, v, sm, bias=bias16, out=o_bias)),
+        "split": loop(split_call),
+        "quantize": loop(lambda: qfa.quantize_qk(q, k, workspace=ws)),
+    }
+    med["bias_bf16"] = variants["bias_bf16"]["median_ms"]
 
     flops_full = 4.0 * B * H * Sq * Sk * D
     tflops = lambda fl, ms: fl / (ms * 1e-3) / 1e12
@@ -278,6 +299,11 @@ def main() -> int:
             "split_ms": round(split_ms, 4),
             "split_over_single_bias": round(split_ms / med["bias_fp32"], 3),
         },
+        "variant_loops": {"warmup": args.variant_warmup, "timed": args.variant_iters, **variants,
+                          "bias_fp32_over_unmasked": round(variants["bias_fp32"]["median_ms"]
+                                                           / variants["unmasked"]["median_ms"], 3),
+                          "split_over_single_bias": round(variants["split"]["median_ms"]
+                                                          / variants["bias_fp32"]["median_ms"], 3)},
         "page_context": {"hardware": "RTX 5090 (comfy-kitchen int8_attention)", **PAGE_MS,
                          "step_tflops": round(page_value, 1)},
         "input_gen_s": round(gen_s, 1),
@@ -388,7 +414,7 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> int:
     f_scale, w_scale = COPY_BYTES / copy_f, COPY_BYTES / copy_w
     un_f, un_w = pick(fetch, UNMASKED_KERNEL) * 1024.0 * f_scale, pick(write, UNMASKED_KERNEL) * 1024.0 * w_scale
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py --cpu-baseline off "
-           "--steps 2 --warmup 1 --variant-iters 1 --copy-calibration")
+           "--steps 2 --warmup 1 --variant-iters 1 --variant-warmup 0 --copy-calibration")
     out = {
         "what": "HBM bytes per launch of the unmasked banded attention call (B1 H56 Sq4096 Sk33600 D128 bf16), "
                 "and of the step's quantize and LSE-merge kernels on the same workload",
