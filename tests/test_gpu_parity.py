@@ -1184,6 +1184,28 @@ def test_debug_log_names_the_instance():
                for x in lines), lines
 
 
+def test_quantize_into_caller_outputs():
+    """quantize_qk(out=...) writes the same bytes into caller-provided (previously garbage-filled)
+    tensors as the allocating call, centred and uncentred, and a second call into the same tensors
+    overwrites every element."""
+    w = W.WORKLOADS["dense4k"]
+    q, k, _ = W.make_qkv(w, H=4, Hkv=2, Sq=333, Sk=517)
+    tq, tk = up(q), up(k)
+    for center in (True, False):
+        ref = qfa.quantize_qk(tq, tk, center_k=center)
+        out = {n: None if t is None else torch.full_like(t, 77 if t.dtype == torch.int8 else float("nan"))
+               for n, t in ref.items()}
+        for _ in range(2):
+            got = qfa.quantize_qk(tq, tk, center_k=center, out=out)
+            for n, t in ref.items():
+                assert (t is None) == (got[n] is None), n
+                if t is not None:
+                    assert got[n].data_ptr() == out[n].data_ptr(), n
+                    assert torch.equal(got[n].view(torch.int8) if t.dtype == torch.int8 else got[n].view(torch.int32),
+                                       t.view(torch.int8) if t.dtype == torch.int8 else t.view(torch.int32)), n
+        assert_quant_equal(got, oracle.quantize_qk(q, k, center_k=center), center)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_kmean_wide_exponent_spans(dtype):
     """K-mean exactness where the kernel's plain fp64 sum is not certified exact: channels mixing values
