@@ -797,8 +797,9 @@ def test_sparse_band_structure():
 # --------------------------------------------------- full-size, sampled rows --
 
 def test_band_full_size_sampled():
-    """B1 H56 Sq4096 Sk33600 D128: unmasked, fp32 bias, bf16 bias and core+skirt split, as timed, on
-    two rows of every 128-row query block of every head."""
+    """B1 H56 Sq4096 Sk33600 D128: unmasked, fp32 bias, bf16 bias and core+skirt split on two rows of
+    every 128-row query block of every head; the single calls both as timed (no LSE) and with the
+    LSE (other kernel instances)."""
     w = W.WORKLOADS["band"]
     q, k, v = W.make_qkv(w)
     core, skirt = w.extras["core"], w.extras["skirt"]
@@ -814,6 +815,9 @@ def test_band_full_size_sampled():
     check_o(o, o_ref, rows, "unmasked")
     check_lse(l, l_ref, rows, "unmasked")
     del o, l
+    o = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt), tv.dtype, "unmasked, no LSE")
+    check_o(o, o_ref, rows, "unmasked, no LSE")
+    del o
     refs = {}
     for dt_b in ("fp32", "bf16"):
         bias = W.bias_tensor(b64, dt_b)
@@ -824,6 +828,10 @@ def test_band_full_size_sampled():
         check_o(o, refs[dt_b][0], rows, f"bias {dt_b}")
         check_lse(l, refs[dt_b][1], rows, f"bias {dt_b}")
         del o, l
+        o = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, bias=tb, out_dtype=dt), tv.dtype,
+                         f"bias {dt_b}, no LSE")
+        check_o(o, refs[dt_b][0], rows, f"bias {dt_b}, no LSE")
+        del o
     # the split of the fp32-bias call: core unmasked + skirts with the bias, merged by LSE
     o_ref, l_ref = refs["fp32"]
     tb = up(W.bias_tensor(b64, "fp32"))
