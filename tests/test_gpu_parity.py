@@ -867,7 +867,8 @@ def test_dense4k_full_size_every_row(lse):
 
 
 def test_d64_full_size_every_row():
-    """B2 H10 S9216 D64 fp16: every row of every (b, h), with the LSE."""
+    """B2 H10 S9216 D64 fp16: every row of every (b, h), with the LSE and without it (the two
+    instances the d64 configuration times)."""
     w = W.WORKLOADS["d64"]
     q, k, v = W.make_qkv(w)
     ref = oracle.quantize_qk(q, k)
@@ -878,6 +879,9 @@ def test_d64_full_size_every_row():
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale)
     check_o(o, o_ref, what="d64 all rows")
     check_lse(l, l_ref, what="d64 all rows")
+    del o, l
+    o = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, out_dtype=dt), tv.dtype, "d64, no LSE")
+    check_o(o, o_ref, what="d64 all rows, no LSE")
 
 
 def test_sparse_full_size_sampled():
