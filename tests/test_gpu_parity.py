@@ -340,6 +340,11 @@ def test_causal_full_size_sampled():
     o_ref, l_ref = oracle.attn(ref, v, w.sm_scale, rows=rows, causal=True)
     check_o(o, o_ref, rows, "causal full")
     check_lse(l, l_ref, rows, "causal full")
+    del o, l
+    # the instance without the LSE, as the dense 4k causal call is timed
+    o = both_outputs(lambda dt: qfa.attn_fwd(g, tv, w.sm_scale, causal=True, out_dtype=dt), tv.dtype,
+                     "causal full, no LSE")
+    check_o(o, o_ref, rows, "causal full, no LSE")
 
 
 GQA_CASES = {
