@@ -320,8 +320,8 @@ def main() -> int:
         ideal = probe_mfma(dev, 3)
         out["roofline"]["measured_compute_only_tile"] = ideal
         out["roofline"]["frac_of_compute_only_tile"] = round(achieved / ideal["tflops"], 4)
-    except (OSError, RuntimeError) as e:
-        out["roofline"]["measured_mfma_ceiling"] = {"error": str(e)[:200]}
+    except Exception as e:   # a measurement add-on: never lose the step line to it
+        out["roofline"]["measured_mfma_ceiling"] = {"error": f"{type(e).__name__}: {str(e)[:200]}"}
 
     # the step's bandwidth-bound calls again, over rotated input sets that do not fit the MALL
     try:
@@ -338,8 +338,8 @@ def main() -> int:
             "quantize_GBps_with_second_k_read": bw["quantize_c4"]["GBps_with_second_k_read"],
             "merge_ms": bw["merge_c4"]["ms"], "merge_GBps": bw["merge_c4"]["GBps"],
             "merge_frac_hbm": bw["merge_c4"]["frac_hbm"]}
-    except RuntimeError as e:
-        out["bandwidth_rotated"] = {"error": str(e)[:200]}
+    except Exception as e:   # a measurement add-on: never lose the step line to it
+        out["bandwidth_rotated"] = {"error": f"{type(e).__name__}: {str(e)[:200]}"}
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
