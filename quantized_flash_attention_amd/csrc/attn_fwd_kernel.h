@@ -355,9 +355,18 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const v16f (&o)[D 
 // or bool keep mask [B|1,H|1,Q,K]: each lane loads its row's 32 values of the
 // tile (8 loads of 16 bytes, 4 keys each) at the start of the tile and adds
 // them after the dequantization, in natural-log units.
+//
+// Occupancy: two blocks per CU (two waves per SIMD) everywhere; at D = 64
+// the LDS ring (40.5 KB) and most instances (154-167 VGPRs) allow three. The
+// causal D = 64 instances need 172-199 VGPRs for their peeled diagonal loop
+// unbounded; bounded to three waves per SIMD they fit 168 (a few bytes of
+// scratch outside the loops) and run 6-8 % faster. BIAS2D instances at D = 64
+// (208-213 VGPRs) stay at two.
 template <int D, int VT, int NW, bool SPARSE, bool HAS_BIAS, bool LSE, bool DUMP = false, bool CAUSAL = false,
           bool QB = false, bool BIAS2D = false>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a, int qtiles, int total_blocks) {
+__global__ __launch_bounds__(NW * 64, (D == 64 && CAUSAL && !BIAS2D) ? 3 : 2) void attn_fwd_kernel(AttnArgs a,
+                                                                                                  int qtiles,
+                                                                                                  int total_blocks) {
   constexpr int BM = 32 * NW;
   constexpr int KC = D / 32;                     // 32-channel blocks of O
   constexpr int NSTG = (QB && D == 128) ? 2 : 3; // LDS stages
